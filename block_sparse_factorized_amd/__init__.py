@@ -1,0 +1,29 @@
+"""Block-sparse causal factorized self-attention (Sparse Transformer strided
+and fixed patterns) for AMD Instinct MI355X (gfx950).
+
+The compute path is libsa.so (C ABI in include/sa.h, HIP kernels in csrc/);
+this package is a thin ctypes binding with the same names.  Importing it
+fails if the library has not been built.
+"""
+from ._binding import (  # noqa: F401
+    EXPORTED,
+    LIB_PATH,
+    PATTERNS,
+    SA_BF16,
+    SA_ERR_ALLOC,
+    SA_ERR_HIP,
+    SA_ERR_INVALID_ARG,
+    SA_ERR_UNSUPPORTED,
+    SA_F32,
+    SA_OK,
+    Layout,
+    SAError,
+    library,
+    sa_bwd,
+    sa_bwd_workspace_size,
+    sa_fwd,
+    sa_layout_build,
+    sa_layout_destroy,
+    sa_layout_export,
+    sa_layout_info,
+)

@@ -1,0 +1,227 @@
+"""ctypes binding of libsa (include/sa.h): argument marshalling only.
+
+Every step of the attention path runs in the library's HIP kernels; torch is
+used here only to allocate device tensors and to name the current stream.
+There is no fallback: if libsa.so is missing, importing this module fails.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Dict, Optional, Sequence, Union
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "_lib", "libsa.so")
+
+SA_OK = 0
+SA_ERR_INVALID_ARG = -1
+SA_ERR_UNSUPPORTED = -2
+SA_ERR_HIP = -3
+SA_ERR_ALLOC = -4
+
+SA_F32 = 0
+SA_BF16 = 1
+
+PATTERNS = {
+    "strided_a": 0,
+    "strided_b": 1,
+    "fixed_a": 2,
+    "fixed_b": 3,
+    "dense": 4,
+}
+
+EXPORTED = [
+    "sa_layout_build", "sa_layout_info", "sa_layout_export", "sa_layout_destroy",
+    "sa_fwd", "sa_bwd", "sa_bwd_workspace_size", "sa_status_string", "sa_last_error",
+]
+
+
+class SAError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__("%s (%d): %s" % (_status_text(status), status, message))
+        self.status = status
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError("libsa.so is not built (%s); run __graft_entry__.build() or "
+                          "python -m block_sparse_factorized_amd._build" % LIB_PATH)
+    lib = ctypes.CDLL(LIB_PATH)
+    i32, i64, vp, cint, flt = ctypes.c_int32, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int, ctypes.c_float
+    sz = ctypes.c_size_t
+    lib.sa_layout_build.argtypes = [cint, i64, i64, i64, i32, ctypes.POINTER(vp)]
+    lib.sa_layout_build.restype = cint
+    lib.sa_layout_info.argtypes = [vp] + [ctypes.POINTER(i64)] * 4
+    lib.sa_layout_info.restype = cint
+    lib.sa_layout_export.argtypes = [vp] * 8
+    lib.sa_layout_export.restype = cint
+    lib.sa_layout_destroy.argtypes = [vp]
+    lib.sa_layout_destroy.restype = None
+    lib.sa_fwd.argtypes = [vp, i32, i32, i64, i32, cint, flt, vp, vp, vp, vp, vp, vp]
+    lib.sa_fwd.restype = cint
+    lib.sa_bwd_workspace_size.argtypes = [i32, i32, i64, i32]
+    lib.sa_bwd_workspace_size.restype = sz
+    lib.sa_bwd.argtypes = [vp, i32, i32, i64, i32, cint, flt] + [vp] * 10 + [sz, vp]
+    lib.sa_bwd.restype = cint
+    lib.sa_status_string.argtypes = [cint]
+    lib.sa_status_string.restype = ctypes.c_char_p
+    lib.sa_last_error.argtypes = []
+    lib.sa_last_error.restype = ctypes.c_char_p
+    return lib
+
+
+_lib = _load()
+
+
+def library():
+    """The loaded ctypes CDLL (for tests that call the C ABI directly)."""
+    return _lib
+
+
+def _status_text(status: int) -> str:
+    return _lib.sa_status_string(status).decode()
+
+
+def _check(status: int):
+    if status != SA_OK:
+        raise SAError(status, _lib.sa_last_error().decode())
+
+
+class Layout:
+    """Owning handle of an sa_layout_t."""
+
+    def __init__(self, handle: int, pattern: str, n: int, l: int, c: int, block: int):
+        self.handle = ctypes.c_void_p(handle)
+        self.pattern, self.n, self.l, self.c, self.block = pattern, n, l, c, block
+
+    def info(self) -> Dict[str, int]:
+        vals = [ctypes.c_int64() for _ in range(4)]
+        _check(_lib.sa_layout_info(self.handle, *[ctypes.byref(v) for v in vals]))
+        return dict(zip(["nqb", "nnz", "n_masks", "allowed"], [v.value for v in vals]))
+
+    def export(self) -> Dict[str, np.ndarray]:
+        inf = self.info()
+        nqb, nnz, nm = inf["nqb"], inf["nnz"], inf["n_masks"]
+        nw = self.block * self.block // 64
+        out = {
+            "row_ptr": np.zeros(nqb + 1, np.int32), "col_idx": np.zeros(max(nnz, 1), np.int32),
+            "mask_id": np.zeros(max(nnz, 1), np.int32),
+            "mask_words": np.zeros((max(nm, 1), nw), np.uint64),
+            "col_ptr": np.zeros(nqb + 1, np.int32), "row_idx": np.zeros(max(nnz, 1), np.int32),
+            "csr_pos": np.zeros(max(nnz, 1), np.int32),
+        }
+        order = ["row_ptr", "col_idx", "mask_id", "mask_words", "col_ptr", "row_idx", "csr_pos"]
+        _check(_lib.sa_layout_export(self.handle, *[ctypes.c_void_p(out[k].ctypes.data) for k in order]))
+        for k in ("col_idx", "mask_id", "row_idx", "csr_pos"):
+            out[k] = out[k][:nnz]
+        out["mask_words"] = out["mask_words"][:nm]
+        return out
+
+    def close(self):
+        if self.handle is not None and self.handle.value:
+            _lib.sa_layout_destroy(self.handle)
+        self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+def sa_layout_build(pattern: Union[str, int], n: int, l: int, c: int = 1, block: int = 64) -> Layout:
+    pid = PATTERNS[pattern] if isinstance(pattern, str) else int(pattern)
+    h = ctypes.c_void_p()
+    _check(_lib.sa_layout_build(pid, n, l, c, block, ctypes.byref(h)))
+    return Layout(h.value, pattern, n, l, c, block)
+
+
+def sa_layout_info(layout: Layout) -> Dict[str, int]:
+    return layout.info()
+
+
+def sa_layout_export(layout: Layout) -> Dict[str, np.ndarray]:
+    return layout.export()
+
+
+def sa_layout_destroy(layout: Layout) -> None:
+    layout.close()
+
+
+def sa_bwd_workspace_size(B: int, H: int, n: int, d: int) -> int:
+    return int(_lib.sa_bwd_workspace_size(B, H, n, d))
+
+
+def _head_array(layouts, H: int):
+    if isinstance(layouts, Layout):
+        layouts = [layouts] * H
+    if len(layouts) != H:
+        raise ValueError("need one layout per head (%d), got %d" % (H, len(layouts)))
+    arr = (ctypes.c_void_p * H)(*[lay.handle for lay in layouts])
+    return arr
+
+
+def _dtype_code(t) -> int:
+    import torch
+    if t.dtype == torch.float32:
+        return SA_F32
+    if t.dtype == torch.bfloat16:
+        return SA_BF16
+    raise TypeError("dtype %s not supported (float32 or bfloat16)" % t.dtype)
+
+
+def _stream_handle(stream, device):
+    import torch
+    s = stream if stream is not None else torch.cuda.current_stream(device)
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _check_tensor(name, t, shape, dtype, device):
+    if tuple(t.shape) != tuple(shape) or t.dtype != dtype or t.device != device or not t.is_contiguous():
+        raise ValueError("%s must be a contiguous %s tensor of shape %s on %s" % (name, dtype, shape, device))
+
+
+def sa_fwd(q, k, v, layouts: Union[Layout, Sequence[Layout]], scale: float, o=None, lse=None, stream=None):
+    """O, lse = attention over the layouts' allowed pairs.  q, k, v:
+    [B, H, n, d] contiguous CUDA tensors (float32 or bfloat16)."""
+    import torch
+    B, H, n, d = q.shape
+    for name, t in (("k", k), ("v", v)):
+        _check_tensor(name, t, q.shape, q.dtype, q.device)
+    _check_tensor("q", q, q.shape, q.dtype, q.device)
+    if o is None:
+        o = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((B, H, n), dtype=torch.float32, device=q.device)
+    _check_tensor("o", o, q.shape, q.dtype, q.device)
+    _check_tensor("lse", lse, (B, H, n), torch.float32, q.device)
+    heads = _head_array(layouts, H)
+    _check(_lib.sa_fwd(heads, B, H, n, d, _dtype_code(q), float(scale), q.data_ptr(), k.data_ptr(),
+                       v.data_ptr(), o.data_ptr(), lse.data_ptr(), _stream_handle(stream, q.device)))
+    return o, lse
+
+
+def sa_bwd(q, k, v, o, lse, do, layouts: Union[Layout, Sequence[Layout]], scale: float,
+           dq=None, dk=None, dv=None, workspace=None, stream=None):
+    """dQ, dK, dV of L = sum(dO * O), recomputing the weights from lse."""
+    import torch
+    B, H, n, d = q.shape
+    for name, t in (("q", q), ("k", k), ("v", v), ("o", o), ("do", do)):
+        _check_tensor(name, t, q.shape, q.dtype, q.device)
+    _check_tensor("lse", lse, (B, H, n), torch.float32, q.device)
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(q) if dk is None else dk
+    dv = torch.empty_like(q) if dv is None else dv
+    for name, t in (("dq", dq), ("dk", dk), ("dv", dv)):
+        _check_tensor(name, t, q.shape, q.dtype, q.device)
+    ws_bytes = sa_bwd_workspace_size(B, H, n, d)
+    if workspace is None:
+        workspace = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=q.device)
+    heads = _head_array(layouts, H)
+    _check(_lib.sa_bwd(heads, B, H, n, d, _dtype_code(q), float(scale), q.data_ptr(), k.data_ptr(),
+                       v.data_ptr(), o.data_ptr(), lse.data_ptr(), do.data_ptr(), dq.data_ptr(),
+                       dk.data_ptr(), dv.data_ptr(), workspace.data_ptr(), workspace.numel(),
+                       _stream_handle(stream, q.device)))
+    return dq, dk, dv

@@ -1,0 +1,403 @@
+// capi.cpp -- the extern "C" entry points of libsa: argument checks, layout
+// upload, work lists, kernel dispatch and error reporting.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <numeric>
+#include <string>
+#include <vector>
+
+#include "kernel_args.h"
+#include "sa_internal.h"
+
+namespace sa {
+
+namespace {
+thread_local std::string g_last_error;
+}
+
+int fail(int status, const char* fmt, ...)
+{
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_last_error = buf;
+    return status;
+}
+
+namespace {
+
+int hip_fail(hipError_t e, const char* what)
+{
+    return fail(SA_ERR_HIP, "%s: %s (%d)", what, hipGetErrorString(e), (int)e);
+}
+
+// Upload a layout to the current device once; later calls return the view.
+int device_layout(sa_layout* L, int dev, DevLayout* out)
+{
+    std::lock_guard<std::mutex> g(L->mu);
+    auto it = L->dev.find(dev);
+    if (it != L->dev.end()) {
+        *out = it->second;
+        return SA_OK;
+    }
+    const size_t nqb1 = (size_t)L->nqb + 1, nnz = (size_t)L->nnz;
+    const size_t nwords = L->masks.size();
+    // Sections, each 256-byte aligned: masks first (8-byte words).
+    auto al = [](size_t x) { return (x + 255) & ~(size_t)255; };
+    size_t off_masks = 0;
+    size_t off_masks_t = al(off_masks + nwords * 8);
+    size_t off_row_ptr = al(off_masks_t + nwords * 8);
+    size_t off_col_idx = al(off_row_ptr + nqb1 * 4);
+    size_t off_mask_id = al(off_col_idx + nnz * 4);
+    size_t off_col_ptr = al(off_mask_id + nnz * 4);
+    size_t off_row_idx = al(off_col_ptr + nqb1 * 4);
+    size_t off_col_mask = al(off_row_idx + nnz * 4);
+    size_t total = al(off_col_mask + nnz * 4);
+    std::vector<unsigned char> host(total, 0);
+    if (nwords) {
+        memcpy(&host[off_masks], L->masks.data(), nwords * 8);
+        // Transposed copies for kernels that walk a block by key column.
+        const int64_t T = L->T, nw = T * T / 64;
+        uint64_t* mt = (uint64_t*)&host[off_masks_t];
+        for (int64_t m = 0; m < L->n_masks; ++m) {
+            const uint64_t* src = &L->masks[m * nw];
+            uint64_t* dst = mt + m * nw;
+            for (int64_t r = 0; r < T; ++r)
+                for (int64_t s2 = 0; s2 < T; ++s2) {
+                    int64_t e = r * T + s2, f = s2 * T + r;
+                    if ((src[e >> 6] >> (e & 63)) & 1ull) dst[f >> 6] |= 1ull << (f & 63);
+                }
+        }
+    }
+    memcpy(&host[off_row_ptr], L->row_ptr.data(), nqb1 * 4);
+    if (nnz) {
+        memcpy(&host[off_col_idx], L->col_idx.data(), nnz * 4);
+        memcpy(&host[off_mask_id], L->mask_id.data(), nnz * 4);
+        memcpy(&host[off_row_idx], L->row_idx.data(), nnz * 4);
+        std::vector<int32_t> col_mask(nnz);
+        for (size_t a = 0; a < nnz; ++a) col_mask[a] = L->mask_id[L->csr_pos[a]];
+        memcpy(&host[off_col_mask], col_mask.data(), nnz * 4);
+    }
+    memcpy(&host[off_col_ptr], L->col_ptr.data(), nqb1 * 4);
+    void* mem = nullptr;
+    hipError_t e = hipMalloc(&mem, total);
+    if (e != hipSuccess) return fail(SA_ERR_ALLOC, "layout upload: hipMalloc(%zu): %s", total, hipGetErrorString(e));
+    e = hipMemcpy(mem, host.data(), total, hipMemcpyHostToDevice);
+    if (e != hipSuccess) {
+        (void)hipFree(mem);
+        return hip_fail(e, "layout upload: hipMemcpy");
+    }
+    unsigned char* b = (unsigned char*)mem;
+    DevLayout v;
+    v.masks = (const uint64_t*)(b + off_masks);
+    v.masks_t = (const uint64_t*)(b + off_masks_t);
+    v.row_ptr = (const int32_t*)(b + off_row_ptr);
+    v.col_idx = (const int32_t*)(b + off_col_idx);
+    v.mask_id = (const int32_t*)(b + off_mask_id);
+    v.col_ptr = (const int32_t*)(b + off_col_ptr);
+    v.row_idx = (const int32_t*)(b + off_row_idx);
+    v.col_mask = (const int32_t*)(b + off_col_mask);
+    L->dev_mem[dev] = mem;
+    L->dev[dev] = v;
+    *out = v;
+    return SA_OK;
+}
+
+// ---------------------------------------------------------------------------
+// Work lists.  One item per (batch*head, block); ordered longest first so the
+// heaviest blocks start early and the tail is made of short ones.  Cached per
+// (kind, device, B, H, layouts).
+enum ListKind { kByQuery = 0, kByKey = 1 };
+
+struct Plan {
+    Item* items;
+    int count;
+};
+
+std::mutex g_plan_mu;
+std::map<std::string, Plan> g_plans;
+
+int get_plan(ListKind kind, int dev, int32_t B, int32_t H, sa_layout* const* hl, Plan* out)
+{
+    std::string key = std::to_string(kind) + ":" + std::to_string(dev) + ":" + std::to_string(B) + ":" +
+                      std::to_string(H);
+    for (int32_t h = 0; h < H; ++h) key += ":" + std::to_string(hl[h]->serial);
+    std::lock_guard<std::mutex> g(g_plan_mu);
+    auto it = g_plans.find(key);
+    if (it != g_plans.end()) {
+        *out = it->second;
+        return SA_OK;
+    }
+    const int64_t nqb = hl[0]->nqb;
+    const int64_t count = (int64_t)B * H * nqb;
+    std::vector<Item> items((size_t)count);
+    std::vector<int32_t> cost((size_t)count);
+    size_t x = 0;
+    for (int32_t bh = 0; bh < B * H; ++bh) {
+        const sa_layout* L = hl[bh % H];
+        const std::vector<int32_t>& ptr = kind == kByQuery ? L->row_ptr : L->col_ptr;
+        for (int64_t blk = 0; blk < nqb; ++blk, ++x) {
+            items[x] = Item{bh, (int32_t)blk};
+            cost[x] = ptr[blk + 1] - ptr[blk];
+        }
+    }
+    std::vector<size_t> order((size_t)count);
+    std::iota(order.begin(), order.end(), 0);
+    std::stable_sort(order.begin(), order.end(), [&](size_t u, size_t v) { return cost[u] > cost[v]; });
+    std::vector<Item> sorted((size_t)count);
+    for (size_t a = 0; a < (size_t)count; ++a) sorted[a] = items[order[a]];
+    void* mem = nullptr;
+    hipError_t e = hipMalloc(&mem, sorted.size() * sizeof(Item));
+    if (e != hipSuccess) return fail(SA_ERR_ALLOC, "work list: hipMalloc: %s", hipGetErrorString(e));
+    e = hipMemcpy(mem, sorted.data(), sorted.size() * sizeof(Item), hipMemcpyHostToDevice);
+    if (e != hipSuccess) {
+        (void)hipFree(mem);
+        return hip_fail(e, "work list: hipMemcpy");
+    }
+    Plan p{(Item*)mem, (int)count};
+    g_plans[key] = p;
+    *out = p;
+    return SA_OK;
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15) == 0; }
+
+// Checks shared by sa_fwd and sa_bwd; fills the head table.
+int common_checks(const char* fn, const sa_layout_t* const* head_layout, int32_t B, int32_t H, int64_t n,
+                  int32_t d, int dtype, float scale, bool backward, HeadTable* ht, std::vector<sa_layout*>* hl,
+                  sa_layout** distinct_out, int* n_distinct)
+{
+    if (!head_layout) return fail(SA_ERR_INVALID_ARG, "%s: head_layout is NULL", fn);
+    if (B < 1 || H < 1) return fail(SA_ERR_INVALID_ARG, "%s: B = %d, H = %d must be >= 1", fn, B, H);
+    if (H > kMaxHeads) return fail(SA_ERR_INVALID_ARG, "%s: H = %d exceeds %d", fn, H, kMaxHeads);
+    if (n < 1 || d < 1) return fail(SA_ERR_INVALID_ARG, "%s: n = %lld, d = %d must be >= 1", fn, (long long)n, d);
+    if (dtype != SA_F32 && dtype != SA_BF16) return fail(SA_ERR_INVALID_ARG, "%s: unknown dtype %d", fn, dtype);
+    if (!std::isfinite(scale) || !(scale > 0.f))
+        return fail(SA_ERR_INVALID_ARG, "%s: scale must be finite and > 0", fn);
+    const int32_t block = dtype == SA_F32 ? 16 : 64;
+    bool ok;
+    if (dtype == SA_F32)
+        ok = !backward && d == 64;
+    else
+        ok = d == 64 || d == 128;
+    if (!ok)
+        return fail(SA_ERR_UNSUPPORTED, "%s: no kernel for dtype %s, d = %d%s", fn, dtype == SA_F32 ? "f32" : "bf16", d,
+                    backward && dtype == SA_F32 ? " (backward is bf16 only)" : "");
+    hl->assign(H, nullptr);
+    int nl = 0;
+    sa_layout* distinct[kMaxLayouts];
+    for (int32_t h = 0; h < H; ++h) {
+        sa_layout* L = const_cast<sa_layout*>(head_layout[h]);
+        if (!L) return fail(SA_ERR_INVALID_ARG, "%s: head_layout[%d] is NULL", fn, h);
+        if (L->n != n)
+            return fail(SA_ERR_INVALID_ARG, "%s: head_layout[%d] was built for n = %lld, call has n = %lld", fn, h,
+                        (long long)L->n, (long long)n);
+        if (L->T != block)
+            return fail(SA_ERR_UNSUPPORTED, "%s: head_layout[%d] has block %d; %s kernels need block %d", fn, h, L->T,
+                        dtype == SA_F32 ? "f32" : "bf16", block);
+        int idx = -1;
+        for (int a = 0; a < nl; ++a)
+            if (distinct[a] == L) idx = a;
+        if (idx < 0) {
+            if (nl == kMaxLayouts)
+                return fail(SA_ERR_INVALID_ARG, "%s: more than %d distinct layouts in one call", fn, kMaxLayouts);
+            distinct[nl] = L;
+            idx = nl++;
+        }
+        ht->head_lay[h] = (uint8_t)idx;
+        (*hl)[h] = L;
+    }
+    if ((int64_t)B * H * (n / block) > (int64_t)1 << 30)
+        return fail(SA_ERR_UNSUPPORTED, "%s: %lld work items is too many for one launch", fn,
+                    (long long)((int64_t)B * H * (n / block)));
+    *n_distinct = nl;
+    for (int a = 0; a < nl; ++a) distinct_out[a] = distinct[a];
+    return SA_OK;
+}
+
+// Device side of a call: current device, layouts uploaded, head table filled.
+int prepare_device(sa_layout* const* distinct, int nl, HeadTable* ht, int* dev_out)
+{
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+    for (int a = 0; a < nl; ++a) {
+        int st = device_layout(distinct[a], dev, &ht->lay[a]);
+        if (st != SA_OK) return st;
+    }
+    for (int a = nl; a < kMaxLayouts; ++a) ht->lay[a] = ht->lay[0];
+    *dev_out = dev;
+    return SA_OK;
+}
+
+}  // namespace
+}  // namespace sa
+
+using namespace sa;
+
+extern "C" {
+
+int sa_layout_build(int pattern, int64_t n, int64_t l, int64_t c, int32_t block, sa_layout_t** out)
+{
+    return build_layout(pattern, n, l, c, block, out);
+}
+
+int sa_layout_info(const sa_layout_t* lay, int64_t* nqb, int64_t* nnz, int64_t* n_masks, int64_t* allowed_pairs)
+{
+    if (!lay) return fail(SA_ERR_INVALID_ARG, "sa_layout_info: layout is NULL");
+    if (nqb) *nqb = lay->nqb;
+    if (nnz) *nnz = lay->nnz;
+    if (n_masks) *n_masks = lay->n_masks;
+    if (allowed_pairs) *allowed_pairs = lay->allowed;
+    return SA_OK;
+}
+
+int sa_layout_export(const sa_layout_t* lay, int32_t* row_ptr, int32_t* col_idx, int32_t* mask_id,
+                     uint64_t* mask_words, int32_t* col_ptr, int32_t* row_idx, int32_t* csr_pos)
+{
+    if (!lay) return fail(SA_ERR_INVALID_ARG, "sa_layout_export: layout is NULL");
+    auto cp = [](void* dst, const void* src, size_t bytes) {
+        if (dst && bytes) memcpy(dst, src, bytes);
+    };
+    cp(row_ptr, lay->row_ptr.data(), lay->row_ptr.size() * 4);
+    cp(col_idx, lay->col_idx.data(), lay->col_idx.size() * 4);
+    cp(mask_id, lay->mask_id.data(), lay->mask_id.size() * 4);
+    cp(mask_words, lay->masks.data(), lay->masks.size() * 8);
+    cp(col_ptr, lay->col_ptr.data(), lay->col_ptr.size() * 4);
+    cp(row_idx, lay->row_idx.data(), lay->row_idx.size() * 4);
+    cp(csr_pos, lay->csr_pos.data(), lay->csr_pos.size() * 4);
+    return SA_OK;
+}
+
+void sa_layout_destroy(sa_layout_t* lay)
+{
+    if (!lay) return;
+    for (auto& kv : lay->dev_mem) {
+        int cur = 0;
+        if (hipGetDevice(&cur) == hipSuccess && hipSetDevice(kv.first) == hipSuccess) {
+            (void)hipFree(kv.second);
+            (void)hipSetDevice(cur);
+        }
+    }
+    delete lay;
+}
+
+int sa_fwd(const sa_layout_t* const* head_layout, int32_t B, int32_t H, int64_t n, int32_t d, int dtype,
+           float scale, const void* q, const void* k, const void* v, void* o, float* lse, void* stream)
+{
+    HeadTable ht;
+    int dev = 0, nl = 0;
+    std::vector<sa_layout*> hl;
+    sa_layout* distinct[kMaxLayouts];
+    int st = common_checks("sa_fwd", head_layout, B, H, n, d, dtype, scale, false, &ht, &hl, distinct, &nl);
+    if (st != SA_OK) return st;
+    if (!q || !k || !v || !o || !lse) return fail(SA_ERR_INVALID_ARG, "sa_fwd: NULL tensor pointer");
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || ((uintptr_t)lse & 3))
+        return fail(SA_ERR_INVALID_ARG, "sa_fwd: q, k, v, o must be 16-byte aligned, lse 4-byte aligned");
+    st = prepare_device(distinct, nl, &ht, &dev);
+    if (st != SA_OK) return st;
+    Plan plan;
+    st = get_plan(kByQuery, dev, B, H, hl.data(), &plan);
+    if (st != SA_OK) return st;
+    FwdArgs a;
+    a.q = q;
+    a.k = k;
+    a.v = v;
+    a.o = o;
+    a.lse = lse;
+    a.n = n;
+    a.H = H;
+    a.scale = scale;
+    a.scale_log2 = scale * 1.4426950408889634f;
+    a.items = plan.items;
+    a.heads = ht;
+    hipError_t e = dtype == SA_BF16 ? launch_fwd_bf16_t64(d, a, plan.count, (hipStream_t)stream)
+                                    : launch_fwd_f32_t16(d, a, plan.count, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, "sa_fwd: kernel launch");
+    return SA_OK;
+}
+
+size_t sa_bwd_workspace_size(int32_t B, int32_t H, int64_t n, int32_t d)
+{
+    (void)d;
+    if (B < 1 || H < 1 || n < 1) return 0;
+    return (((size_t)B * H * n * sizeof(float)) + 255) & ~(size_t)255;
+}
+
+int sa_bwd(const sa_layout_t* const* head_layout, int32_t B, int32_t H, int64_t n, int32_t d, int dtype, float scale,
+           const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dout, void* dq,
+           void* dk, void* dv, void* workspace, size_t ws_bytes, void* stream)
+{
+    HeadTable ht;
+    int dev = 0, nl = 0;
+    std::vector<sa_layout*> hl;
+    sa_layout* distinct[kMaxLayouts];
+    int st = common_checks("sa_bwd", head_layout, B, H, n, d, dtype, scale, true, &ht, &hl, distinct, &nl);
+    if (st != SA_OK) return st;
+    if (!q || !k || !v || !o || !lse || !dout || !dq || !dk || !dv || !workspace)
+        return fail(SA_ERR_INVALID_ARG, "sa_bwd: NULL pointer");
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(dout) || !aligned16(dq) ||
+        !aligned16(dk) || !aligned16(dv) || !aligned16(workspace) || ((uintptr_t)lse & 3))
+        return fail(SA_ERR_INVALID_ARG, "sa_bwd: tensors and workspace must be 16-byte aligned, lse 4-byte");
+    if (ws_bytes < sa_bwd_workspace_size(B, H, n, d))
+        return fail(SA_ERR_INVALID_ARG, "sa_bwd: workspace of %zu bytes, %zu needed", ws_bytes,
+                    sa_bwd_workspace_size(B, H, n, d));
+    st = prepare_device(distinct, nl, &ht, &dev);
+    if (st != SA_OK) return st;
+    Plan pk, pq;
+    st = get_plan(kByKey, dev, B, H, hl.data(), &pk);
+    if (st != SA_OK) return st;
+    st = get_plan(kByQuery, dev, B, H, hl.data(), &pq);
+    if (st != SA_OK) return st;
+    BwdArgs a;
+    a.q = q;
+    a.k = k;
+    a.v = v;
+    a.o = o;
+    a.lse = lse;
+    a.dout = dout;
+    a.dq = dq;
+    a.dk = dk;
+    a.dv = dv;
+    a.delta = (float*)workspace;
+    a.n = n;
+    a.H = H;
+    a.BH = B * H;
+    a.scale = scale;
+    a.scale_log2 = scale * 1.4426950408889634f;
+    a.heads = ht;
+    hipStream_t s = (hipStream_t)stream;
+    a.items = nullptr;
+    hipError_t e = launch_bwd_delta_bf16(d, a, (int64_t)B * H * n, s);
+    if (e != hipSuccess) return hip_fail(e, "sa_bwd: delta kernel launch");
+    a.items = pk.items;
+    e = launch_bwd_dkdv_bf16_t64(d, a, pk.count, s);
+    if (e != hipSuccess) return hip_fail(e, "sa_bwd: dK/dV kernel launch");
+    a.items = pq.items;
+    e = launch_bwd_dq_bf16_t64(d, a, pq.count, s);
+    if (e != hipSuccess) return hip_fail(e, "sa_bwd: dQ kernel launch");
+    return SA_OK;
+}
+
+const char* sa_status_string(int status)
+{
+    switch (status) {
+    case SA_OK: return "ok";
+    case SA_ERR_INVALID_ARG: return "invalid argument";
+    case SA_ERR_UNSUPPORTED: return "unsupported combination";
+    case SA_ERR_HIP: return "HIP runtime error";
+    case SA_ERR_ALLOC: return "allocation failed";
+    default: return "unknown status";
+    }
+}
+
+const char* sa_last_error(void) { return g_last_error.c_str(); }
+
+}  // extern "C"

@@ -1,0 +1,65 @@
+// kernel_args.h -- argument blocks passed by value to the libsa kernels and
+// the host-side launchers (defined in the .hip files).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "sa_internal.h"
+
+namespace sa {
+
+// One (batch*H + head, block) work item; y is a query block for the forward
+// and dQ kernels and a key block for the dK/dV kernel.
+struct Item {
+    int32_t bh;
+    int32_t blk;
+};
+
+struct HeadTable {
+    DevLayout lay[kMaxLayouts];
+    uint8_t head_lay[kMaxHeads];  // head -> index into lay
+};
+
+struct FwdArgs {
+    const void* q;
+    const void* k;
+    const void* v;
+    void* o;
+    float* lse;
+    int64_t n;
+    int32_t H;
+    float scale;       // score scale
+    float scale_log2;  // scale * log2(e)
+    const Item* items;
+    HeadTable heads;
+};
+
+struct BwdArgs {
+    const void* q;
+    const void* k;
+    const void* v;
+    const void* o;
+    const float* lse;
+    const void* dout;
+    void* dq;
+    void* dk;
+    void* dv;
+    float* delta;  // workspace: D_i = sum_t dO_it * O_it, fp32 [B*H*n]
+    int64_t n;
+    int32_t H;
+    int32_t BH;
+    float scale;
+    float scale_log2;
+    const Item* items;  // work list of the launch
+    HeadTable heads;
+};
+
+// Launchers: enqueue one kernel on `stream`, return hipGetLastError().
+hipError_t launch_fwd_bf16_t64(int d, const FwdArgs& a, int n_items, hipStream_t stream);
+hipError_t launch_fwd_f32_t16(int d, const FwdArgs& a, int n_items, hipStream_t stream);
+hipError_t launch_bwd_delta_bf16(int d, const BwdArgs& a, int64_t rows, hipStream_t stream);
+hipError_t launch_bwd_dkdv_bf16_t64(int d, const BwdArgs& a, int n_items, hipStream_t stream);
+hipError_t launch_bwd_dq_bf16_t64(int d, const BwdArgs& a, int n_items, hipStream_t stream);
+
+}  // namespace sa

@@ -1,0 +1,216 @@
+// layout.cpp -- host builder of block layouts for the factorized patterns.
+//
+// "OpenAI Sparse Transformer" (agentlenshq.com), "Implementation and
+// Limitations", and pcnews.ru, "Релиз кода": sparse attention is executed by
+// slicing the query and key matrices into blocks and computing only the
+// blocks that hold allowed pairs.  The patterns ("Factorized Attention
+// Patterns"; pcnews.ru, "Разреженное внимание") are, for key j <= query i:
+//   strided A  0 <= i-j < l           strided B  (i-j) mod l == 0
+//   fixed A    floor(j/l) == floor(i/l)   fixed B  j mod l >= l-c
+//   dense causal: every j <= i.
+//
+// For a block row (query rows i0..i0+T-1) each row's allowed keys inside a
+// key block are a run of intervals (strided A, fixed A, fixed B, dense) or an
+// arithmetic progression with step l (strided B), so a block's mask is
+// written row by row without testing every element.  Key blocks that cannot
+// hold a pair are skipped by a per-pattern range or test first.
+#include <algorithm>
+#include <cstring>
+#include <new>
+#include <unordered_map>
+
+#include "sa_internal.h"
+
+namespace sa {
+namespace {
+
+struct Params {
+    int pattern;
+    int64_t l, c, T;
+};
+
+inline void set_bits(uint64_t* w, int64_t e0, int64_t e1)  // bits [e0, e1]
+{
+    while (e0 <= e1) {
+        int64_t word = e0 >> 6, b0 = e0 & 63;
+        int64_t b1 = std::min<int64_t>(63, b0 + (e1 - e0));
+        int64_t len = b1 - b0 + 1;
+        uint64_t m = (len == 64) ? ~0ull : (((1ull << len) - 1) << b0);
+        w[word] |= m;
+        e0 += len;
+    }
+}
+
+// Allowed keys of query i inside [j0, j1] (j1 <= i), as bits of tile row r.
+// Returns the number of allowed keys.
+int64_t row_bits(const Params& p, int64_t i, int64_t j0, int64_t j1, int64_t r, uint64_t* w)
+{
+    const int64_t base = r * p.T - j0;  // element index of key j is base + j
+    int64_t cnt = 0;
+    auto run = [&](int64_t a, int64_t b) {
+        if (a > b) return;
+        set_bits(w, base + a, base + b);
+        cnt += b - a + 1;
+    };
+    switch (p.pattern) {
+    case SA_STRIDED_A: run(std::max(j0, i - p.l + 1), j1); break;
+    case SA_STRIDED_B: {
+        int64_t r0 = (i - j1) % p.l;
+        for (int64_t j = j1 - (p.l - r0) % p.l; j >= j0; j -= p.l) run(j, j);
+        break;
+    }
+    case SA_FIXED_A: run(std::max(j0, p.l * (i / p.l)), j1); break;
+    case SA_FIXED_B:
+        for (int64_t m = j0 / p.l; m <= j1 / p.l; ++m)
+            run(std::max(j0, m * p.l + p.l - p.c), std::min(j1, m * p.l + p.l - 1));
+        break;
+    default: run(j0, j1); break;
+    }
+    return cnt;
+}
+
+// Could key block kb hold a pair for query block qb?  (A cheap filter; the
+// row pass below is exact.)
+bool may_hold(const Params& p, int64_t qb, int64_t kb)
+{
+    const int64_t T = p.T;
+    switch (p.pattern) {
+    case SA_STRIDED_B: {
+        int64_t lo = std::max<int64_t>(0, (qb - kb) * T - (T - 1));
+        int64_t hi = (qb - kb) * T + (T - 1);
+        return (hi / p.l) * p.l >= lo;
+    }
+    case SA_FIXED_B: {
+        int64_t j0 = kb * T, j1 = std::min(kb * T + T - 1, qb * T + T - 1);
+        int64_t off = j0 % p.l;
+        int64_t first = off >= p.l - p.c ? j0 : j0 + (p.l - p.c - off);
+        return first <= j1;
+    }
+    default: return true;
+    }
+}
+
+int64_t first_key_block(const Params& p, int64_t qb)
+{
+    const int64_t i0 = qb * p.T;
+    switch (p.pattern) {
+    case SA_STRIDED_A: return std::max<int64_t>(0, i0 - (p.l - 1)) / p.T;
+    case SA_FIXED_A: return (p.l * (i0 / p.l)) / p.T;
+    default: return 0;
+    }
+}
+
+struct VecHash {
+    size_t operator()(const std::vector<uint64_t>& v) const
+    {
+        uint64_t h = 1469598103934665603ull;
+        for (uint64_t x : v) {
+            h ^= x + 0x9e3779b97f4a7c15ull + (h << 6) + (h >> 2);
+            h *= 1099511628211ull;
+        }
+        return (size_t)h;
+    }
+};
+
+uint64_t next_serial()
+{
+    static std::mutex mu;
+    static uint64_t s = 0;
+    std::lock_guard<std::mutex> g(mu);
+    return ++s;
+}
+
+}  // namespace
+
+int build_layout(int pattern, int64_t n, int64_t l, int64_t c, int32_t block, sa_layout** out)
+{
+    if (!out) return fail(SA_ERR_INVALID_ARG, "sa_layout_build: out is NULL");
+    *out = nullptr;
+    if (pattern < SA_STRIDED_A || pattern > SA_DENSE_CAUSAL)
+        return fail(SA_ERR_INVALID_ARG, "sa_layout_build: unknown pattern %d", pattern);
+    if (block != 8 && block != 16 && block != 32 && block != 64 && block != 128)
+        return fail(SA_ERR_INVALID_ARG, "sa_layout_build: block %d not in {8,16,32,64,128}", block);
+    if (n < 1) return fail(SA_ERR_INVALID_ARG, "sa_layout_build: n = %lld < 1", (long long)n);
+    if (n % block != 0)
+        return fail(SA_ERR_INVALID_ARG, "sa_layout_build: n = %lld is not a multiple of block %d",
+                    (long long)n, block);
+    if (l < 1) return fail(SA_ERR_INVALID_ARG, "sa_layout_build: l = %lld < 1", (long long)l);
+    if (pattern == SA_FIXED_B && (c < 1 || c > l))
+        return fail(SA_ERR_INVALID_ARG, "sa_layout_build: fixed B needs 1 <= c <= l (c = %lld, l = %lld)",
+                    (long long)c, (long long)l);
+    const int64_t nqb = n / block;
+    if (nqb > 46340)  // nqb*nqb must fit in int32 block indices
+        return fail(SA_ERR_INVALID_ARG, "sa_layout_build: %lld query blocks is too many", (long long)nqb);
+
+    sa_layout* L = new (std::nothrow) sa_layout();
+    if (!L) return fail(SA_ERR_ALLOC, "sa_layout_build: out of host memory");
+    try {
+        L->serial = next_serial();
+        L->pattern = pattern;
+        L->n = n;
+        L->l = l;
+        L->c = pattern == SA_FIXED_B ? c : 0;
+        L->T = block;
+        L->nqb = nqb;
+        const Params p{pattern, l, L->c, block};
+        const int64_t T = block, nw = T * T / 64;
+
+        std::unordered_map<std::vector<uint64_t>, int32_t, VecHash> ids;
+        std::vector<uint64_t> tile(nw);
+        L->row_ptr.assign(nqb + 1, 0);
+        int64_t allowed = 0;
+        for (int64_t qb = 0; qb < nqb; ++qb) {
+            for (int64_t kb = first_key_block(p, qb); kb <= qb; ++kb) {
+                if (!may_hold(p, qb, kb)) continue;
+                std::fill(tile.begin(), tile.end(), 0ull);
+                int64_t pop = 0;
+                for (int64_t r = 0; r < T; ++r) {
+                    int64_t i = qb * T + r, j0 = kb * T, j1 = std::min(kb * T + T - 1, i);
+                    if (j1 < j0) continue;
+                    pop += row_bits(p, i, j0, j1, r, tile.data());
+                }
+                if (pop == 0) continue;
+                allowed += pop;
+                int32_t id = -1;
+                if (pop != T * T) {
+                    auto it = ids.find(tile);
+                    if (it == ids.end()) {
+                        id = (int32_t)ids.size();
+                        ids.emplace(tile, id);
+                        L->masks.insert(L->masks.end(), tile.begin(), tile.end());
+                    } else {
+                        id = it->second;
+                    }
+                }
+                L->col_idx.push_back((int32_t)kb);
+                L->mask_id.push_back(id);
+            }
+            L->row_ptr[qb + 1] = (int32_t)L->col_idx.size();
+        }
+        L->nnz = (int64_t)L->col_idx.size();
+        L->n_masks = (int64_t)ids.size();
+        L->allowed = allowed;
+
+        // Transpose: per key block, its query blocks in ascending order.
+        L->col_ptr.assign(nqb + 1, 0);
+        for (int32_t kb : L->col_idx) L->col_ptr[kb + 1]++;
+        for (int64_t kb = 0; kb < nqb; ++kb) L->col_ptr[kb + 1] += L->col_ptr[kb];
+        L->row_idx.assign(L->nnz, 0);
+        L->csr_pos.assign(L->nnz, 0);
+        std::vector<int32_t> fillp(L->col_ptr.begin(), L->col_ptr.end() - 1);
+        for (int64_t qb = 0; qb < nqb; ++qb)
+            for (int32_t a = L->row_ptr[qb]; a < L->row_ptr[qb + 1]; ++a) {
+                int32_t kb = L->col_idx[a];
+                int32_t slot = fillp[kb]++;
+                L->row_idx[slot] = (int32_t)qb;
+                L->csr_pos[slot] = a;
+            }
+    } catch (const std::bad_alloc&) {
+        delete L;
+        return fail(SA_ERR_ALLOC, "sa_layout_build: out of host memory");
+    }
+    *out = L;
+    return SA_OK;
+}
+
+}  // namespace sa

@@ -1,0 +1,57 @@
+// sa_internal.h -- shared host/device declarations of libsa (not installed).
+#pragma once
+
+#include <stdint.h>
+
+#include <map>
+#include <mutex>
+#include <string>
+#include <vector>
+
+#include "../../include/sa.h"
+
+namespace sa {
+
+constexpr int kMaxLayouts = 8;   // distinct layouts per call
+constexpr int kMaxHeads = 256;   // heads per call
+
+// Device view of one layout: one allocation, several arrays.
+struct DevLayout {
+    const int32_t* row_ptr;   // [nqb+1]   listing by query block
+    const int32_t* col_idx;   // [nnz]     key blocks, ascending per query block
+    const int32_t* mask_id;   // [nnz]     -1 = full block
+    const uint64_t* masks;    // [n_masks][T*T/64]  element (r, s): bit r*T+s
+    const uint64_t* masks_t;  // [n_masks][T*T/64]  the same masks transposed:
+                              //                    element (r, s): bit s*T+r
+    const int32_t* col_ptr;   // [nqb+1]   listing by key block
+    const int32_t* row_idx;   // [nnz]     query blocks, ascending per key block
+    const int32_t* col_mask;  // [nnz]     mask id of each transposed entry
+};
+
+}  // namespace sa
+
+struct sa_layout {
+    uint64_t serial;  // unique per build, keys the work-list cache
+    int pattern;
+    int64_t n, l, c;
+    int32_t T;
+    int64_t nqb, nnz, n_masks, allowed;
+    std::vector<int32_t> row_ptr, col_idx, mask_id;
+    std::vector<uint64_t> masks;
+    std::vector<int32_t> col_ptr, row_idx, csr_pos;
+
+    std::mutex mu;                       // guards dev
+    std::map<int, void*> dev_mem;        // device id -> allocation
+    std::map<int, sa::DevLayout> dev;    // device id -> view
+};
+
+namespace sa {
+
+// Layout builder (host only, layout.cpp).
+int build_layout(int pattern, int64_t n, int64_t l, int64_t c, int32_t block, sa_layout** out);
+
+// Error reporting (capi.cpp): records the message for sa_last_error and
+// returns `status`.
+int fail(int status, const char* fmt, ...);
+
+}  // namespace sa

@@ -1,0 +1,179 @@
+/*
+ * sa.h -- C ABI of libsa: block-sparse causal factorized self-attention
+ * (Sparse Transformer strided and fixed patterns) on AMD Instinct MI355X
+ * (gfx950).
+ *
+ * The operation (sources, by page title and section):
+ *   - "OpenAI Sparse Transformer" (agentlenshq.com), "Sparse Attention and
+ *     Algorithmic Complexity": each output position attends only a subset of
+ *     the input positions, so the cost falls from O(N^2) to O(N sqrt N).
+ *   - same page, "Factorized Attention Patterns", and "Генеративное
+ *     моделирование с разреженными трансформерами" (pcnews.ru),
+ *     "Разреженное внимание": the strided pattern (row and column) and the
+ *     fixed pattern (a fixed column plus the elements after the latest column
+ *     element), each split over two heads.  With i the query position and
+ *     j <= i the key position:
+ *         SA_STRIDED_A   0 <= i - j < l
+ *         SA_STRIDED_B   (i - j) mod l == 0
+ *         SA_FIXED_A     floor(j / l) == floor(i / l)
+ *         SA_FIXED_B     j mod l >= l - c
+ *         SA_DENSE_CAUSAL  every j <= i (the full attention the pages compare
+ *                          sparse attention against)
+ *   - "OpenAI Sparse Transformer", "Implementation and Limitations", and
+ *     pcnews.ru, "Релиз кода": the query and key matrices are sliced into
+ *     blocks and only the needed blocks are computed; the block size sets
+ *     the granularity of the sparsity ("희소 어텐션 (Sparse Attention)",
+ *     molayo1419.me).
+ *   - "희소 어텐션 (Sparse Attention)": scores are query-key dot products,
+ *     normalised by a softmax so that each row of weights sums to one.
+ *   - "[논문 리뷰] Generating Long Sequences with Sparse Transformers"
+ *     (nubint.ai), ABSTRACT item (b): the backward pass recomputes the
+ *     attention matrix rather than storing it; only O and the row
+ *     log-sum-exp are kept from the forward pass.
+ *
+ * Forward, per (batch b, head h, query row i), with S_i the allowed keys of
+ * row i under head h's layout:
+ *     s_ij  = scale * (q_i . k_j)
+ *     lse_i = log(sum_{j in S_i} exp(s_ij))           (natural log, fp32)
+ *     o_i   = sum_{j in S_i} exp(s_ij - lse_i) v_j
+ * A row with S_i empty gets o_i = 0 and lse_i = -inf.  Backward returns the
+ * gradients of L = sum(dO * O) with respect to q, k and v.
+ *
+ * Tensors.  q, k, v, o, dout, dq, dk, dv are device pointers to contiguous
+ * row-major [B][H][n][d] arrays of the call's dtype (16-byte aligned); lse is
+ * a device pointer to fp32 [B][H][n].  All tensor memory is owned by the
+ * caller.  Layouts are owned by the library.
+ *
+ * Execution.  sa_fwd and sa_bwd validate their arguments on the host and
+ * return a negative status without launching anything when a check fails.
+ * Otherwise they enqueue kernels on `stream` (a hipStream_t; NULL is the
+ * default stream) and return SA_OK; device faults surface at the caller's
+ * next synchronisation.  The first call with a new (B, H, layouts)
+ * combination allocates and uploads a small work list (synchronously);
+ * later calls reuse it.  Calls are thread-safe.
+ *
+ * Compiled (dtype, block, d) combinations:
+ *     forward   (SA_F32, 16, 64), (SA_BF16, 64, 64), (SA_BF16, 64, 128)
+ *     backward  (SA_BF16, 64, 64), (SA_BF16, 64, 128)
+ * Others return SA_ERR_UNSUPPORTED.  bf16 calls accumulate in fp32 and
+ * round results to bf16 (nearest even); the softmax weights are rounded to
+ * bf16 before they multiply V.
+ */
+#ifndef SA_H
+#define SA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum sa_pattern {
+    SA_STRIDED_A = 0,
+    SA_STRIDED_B = 1,
+    SA_FIXED_A = 2,
+    SA_FIXED_B = 3,
+    SA_DENSE_CAUSAL = 4
+} sa_pattern_t;
+
+typedef enum sa_dtype { SA_F32 = 0, SA_BF16 = 1 } sa_dtype_t;
+
+enum {
+    SA_OK = 0,
+    SA_ERR_INVALID_ARG = -1, /* a bad value, shape, pointer or alignment */
+    SA_ERR_UNSUPPORTED = -2, /* a valid request with no compiled kernel  */
+    SA_ERR_HIP = -3,         /* the HIP runtime reported an error        */
+    SA_ERR_ALLOC = -4        /* host or device allocation failed         */
+};
+
+/* Opaque block layout of one pattern at one sequence length. */
+typedef struct sa_layout sa_layout_t;
+
+/*
+ * Build the block layout of `pattern` for sequence length n, stride l,
+ * summary width c (used by SA_FIXED_B only) and block size `block`.
+ * Host only.  For every query block qb (rows qb*block .. qb*block+block-1)
+ * it lists, in ascending order, every key block kb holding at least one
+ * allowed (i, j), and gives each listed block an element mask: -1 when every
+ * element is allowed ("full"), else the index of a T*T-bit mask in a
+ * deduplicated table (ids in order of first appearance in the listing).
+ * It also builds the transpose (per key block, its query blocks).
+ *
+ * Errors (SA_ERR_INVALID_ARG): out == NULL; unknown pattern; n < 1;
+ * block not in {8, 16, 32, 64, 128}; n % block != 0; l < 1; for SA_FIXED_B
+ * c < 1 or c > l; nqb*nqb (the block grid) beyond 2^31.  SA_ERR_ALLOC when
+ * memory runs out.  On success *out owns the layout until sa_layout_destroy.
+ */
+int sa_layout_build(int pattern, int64_t n, int64_t l, int64_t c, int32_t block,
+                    sa_layout_t** out);
+
+/*
+ * Sizes of a layout: number of query blocks, listed blocks (nnz), distinct
+ * partial masks, and allowed (i, j) pairs in total.  Any output pointer may
+ * be NULL.  SA_ERR_INVALID_ARG when lay == NULL.
+ */
+int sa_layout_info(const sa_layout_t* lay, int64_t* nqb, int64_t* nnz, int64_t* n_masks,
+                   int64_t* allowed_pairs);
+
+/*
+ * Copy a layout into caller-allocated host arrays (any may be NULL):
+ *   row_ptr[nqb+1], col_idx[nnz], mask_id[nnz]          listing by query block
+ *   mask_words[n_masks * block*block/64]                 mask table; element
+ *        (r, s) of a block (query row r, key column s) is bit (r*block+s)%64
+ *        of word (r*block+s)/64 of its mask, row-major
+ *   col_ptr[nqb+1], row_idx[nnz], csr_pos[nnz]          transpose: for key
+ *        block kb, its query blocks ascending and their positions in the
+ *        listing by query block
+ */
+int sa_layout_export(const sa_layout_t* lay, int32_t* row_ptr, int32_t* col_idx,
+                     int32_t* mask_id, uint64_t* mask_words, int32_t* col_ptr,
+                     int32_t* row_idx, int32_t* csr_pos);
+
+/* Free a layout and its device copies.  NULL is ignored.  The caller must
+ * make sure no enqueued sa_fwd/sa_bwd still uses it. */
+void sa_layout_destroy(sa_layout_t* lay);
+
+/*
+ * Forward pass.  head_layout[h] (h < H) is the layout of head h; several
+ * heads may share one layout, at most 8 distinct layouts per call, H <= 256.
+ * Every layout must have sequence length n and the call's block size
+ * (16 for SA_F32, 64 for SA_BF16).  scale must be finite and > 0.
+ * Writes o [B][H][n][d] (dtype) and lse [B][H][n] (fp32).
+ * Errors: SA_ERR_INVALID_ARG for NULL/misaligned pointers, B < 1, H < 1,
+ * H > 256, a layout whose n differs, a bad scale, more than 8 distinct
+ * layouts; SA_ERR_UNSUPPORTED for a (dtype, block, d) not compiled;
+ * SA_ERR_HIP if a HIP call or the launch fails.
+ */
+int sa_fwd(const sa_layout_t* const* head_layout, int32_t B, int32_t H, int64_t n, int32_t d,
+           int dtype, float scale, const void* q, const void* k, const void* v, void* o,
+           float* lse, void* stream);
+
+/* Bytes of device workspace sa_bwd needs (the fp32 row terms D_i). */
+size_t sa_bwd_workspace_size(int32_t B, int32_t H, int64_t n, int32_t d);
+
+/*
+ * Backward pass (recomputes the attention weights from q, k and lse).
+ * o and lse are sa_fwd's outputs for the same inputs; dout is dL/dO.
+ * Writes dq, dk, dv [B][H][n][d] (dtype).  workspace: device memory of at
+ * least sa_bwd_workspace_size(...) bytes, 16-byte aligned, owned by the
+ * caller, contents ignored on entry.  Same errors as sa_fwd, plus
+ * SA_ERR_INVALID_ARG when ws_bytes is too small.  Deterministic: no atomics,
+ * so equal inputs give bitwise equal outputs.
+ */
+int sa_bwd(const sa_layout_t* const* head_layout, int32_t B, int32_t H, int64_t n, int32_t d,
+           int dtype, float scale, const void* q, const void* k, const void* v, const void* o,
+           const float* lse, const void* dout, void* dq, void* dk, void* dv, void* workspace,
+           size_t ws_bytes, void* stream);
+
+/* Static text of a status code. */
+const char* sa_status_string(int status);
+
+/* Text of the last error raised on the calling thread ("" if none). */
+const char* sa_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SA_H */
