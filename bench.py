@@ -1,0 +1,256 @@
+"""Throughput of block-sparse factorized attention, forward + backward, on one GPU.
+
+A step is one pass of the whole path over one batch of synthetic input:
+sa_fwd (O, lse) followed by sa_bwd (dQ, dK, dV), with inputs already resident
+in HBM.  The layouts are built once before timing (they depend only on the
+pattern, the length and the block size); their build time is reported.
+
+Metric: effective TFLOP/s counted over allowed blocks -- every listed T x T
+block counts 4*T*T*d flops forward and 2.5 times that backward, whether or
+not all of its elements are allowed -- and its fraction of the MI355X dense
+bf16 MFMA peak (2.5 PFLOP/s).
+
+Prints one JSON line.  --gpus above 1 is refused: this build runs on one GPU.
+"""
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "sparse-attn fwd(+bwd) effective TFLOP/s over allowed blocks; % of MFMA peak"
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_F32_TFLOPS = 157.3     # MI355X fp32 (matrix and vector)
+PEAK_HBM_GBS = 8000.0
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="img64",
+                    help="tiny | img32 | text | img64 | audio (default img64, N=12288)")
+    ap.add_argument("--dense", action="store_true", help="run the dense causal comparison layout")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-heads", type=int, default=0,
+                    help="heads in the oracle sample (default: sized to ~10-30 s)")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 512 MiB device copy 5 times (to scale HBM counters)")
+    return ap.parse_args()
+
+
+def copy_calibration():
+    """A plain copy of known size, profiled with the same counters as the
+    kernels so that FETCH_SIZE / WRITE_SIZE can be scaled to bytes."""
+    import torch
+    nbytes = 512 << 20
+    a = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda:0")
+    b = torch.empty_like(a)
+    for _ in range(5):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes_read": nbytes, "copy_bytes_written": nbytes, "launches": 5}), flush=True)
+
+
+def traffic_from_profile(kernel_file, kernel, workload):
+    """HBM bytes per launch measured by the counter runs under profiles/, if
+    they were taken on the current source of the kernel's file (else None)."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    src = os.path.join(ROOT, "block_sparse_factorized_amd", "csrc", kernel_file)
+    if not os.path.exists(path) or not os.path.exists(src):
+        return None
+    sha = hashlib.sha256(open(src, "rb").read()).hexdigest()
+    for e in json.load(open(path)).get("entries", []):
+        if e["kernel"] == kernel and e["workload"] == workload and e["source_sha256"] == sha:
+            return e["hbm_bytes_per_launch"]
+    return None
+
+
+def counted_flops(layouts, batch, T, d):
+    """Forward flops counted over allowed blocks, summed over (batch, head)."""
+    blocks = sum(lay.info()["nnz"] for lay in layouts) * batch
+    return blocks * 4.0 * T * T * d, blocks
+
+
+def cpu_baseline(w, x, pats, T, max_heads):
+    """The fp64 oracle on the host's cores over a bounded sample of heads of
+    the same workload, fwd + bwd, scaled to the same counted-flop metric."""
+    import numpy as np
+    import oracle
+    from workloads import to_f64
+    import block_sparse_factorized_amd as sa
+
+    sample = []
+    for b in range(w.batch):
+        for h in range(w.heads):
+            sample.append((b, h))
+    # interleave A and B heads so any prefix is representative
+    sample.sort(key=lambda bh: (bh[1] // 2, bh[0], bh[1] % 2))
+    sample = sample[:max_heads]
+    counted = 0.0
+    t0 = time.perf_counter()
+    for (b, h) in sample:
+        p, l, c = pats[h]
+        args = [to_f64(x[t][b, h]) for t in ("q", "k", "v", "do")]
+        if w.backward:
+            oracle.head_bwd(p, l, c, *args, 1.0)
+        else:
+            oracle.head_fwd(p, l, c, *args[:3], 1.0)
+        lay = sa.sa_layout_build(p, w.n, l, c, block=T)
+        counted += lay.info()["nnz"] * 4.0 * T * T * w.d * (3.5 if w.backward else 1.0)
+    secs = time.perf_counter() - t0
+    return {
+        "value": counted / secs / 1e12,
+        "unit": "TFLOP/s",
+        "cores": oracle.num_threads(),
+        "kind": "oracle",
+        "sample": "%d of %d heads of %s (b,h in A/B pairs), fwd%s in fp64, %.1f s"
+                  % (len(sample), w.batch * w.heads, w.name, "+bwd" if w.backward else "", secs),
+    }
+
+
+def main():
+    args = parse()
+    if args.copy_calibration:
+        copy_calibration()
+        return
+    if args.gpus != 1:
+        print("bench.py runs on one GPU only: this build has no multi-GPU path "
+              "(--gpus %d refused)" % args.gpus, file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+    import block_sparse_factorized_amd as sa
+    import workloads
+
+    w = workloads.WORKLOADS[args.workload]
+    dev = torch.device("cuda:0")
+    pats = w.head_patterns(dense=args.dense)
+    T, d = w.block, w.d
+
+    t0 = time.perf_counter()
+    cache = {}
+    lays = []
+    for (p, l, c) in pats:
+        if (p, l, c) not in cache:
+            cache[(p, l, c)] = sa.sa_layout_build(p, w.n, l, c, block=T)
+        lays.append(cache[(p, l, c)])
+    layout_ms = (time.perf_counter() - t0) * 1e3
+
+    x = workloads.make_inputs(w)
+    q, k, v, do = (x[t].to(dev) for t in ("q", "k", "v", "do"))
+    o = torch.empty_like(q)
+    lse = torch.empty(q.shape[:3], dtype=torch.float32, device=dev)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(q), torch.empty_like(q)
+    ws = torch.empty(max(sa.sa_bwd_workspace_size(w.batch, w.heads, w.n, d), 16), dtype=torch.uint8, device=dev)
+    scale = 1.0
+
+    # One step = forward + the three backward stages (the same kernels sa_bwd
+    # launches), each bracketed by events on torch's current stream -- the
+    # stream every launch goes to -- so every kernel is timed live.
+    names = ["fwd", "bwd_rowterms", "bwd_dkdv", "bwd_dq"] if w.backward else ["fwd"]
+
+    def step(ev=None):
+        rec = (lambda i: ev[i].record()) if ev is not None else (lambda i: None)
+        rec(0)
+        sa.sa_fwd(q, k, v, lays, scale, o=o, lse=lse)
+        rec(1)
+        if w.backward:
+            sa.sa_bwd_rowterms(o, do, lays, scale, workspace=ws)
+            rec(2)
+            sa.sa_bwd_dkdv(q, k, v, lse, do, lays, scale, ws, dk=dk, dv=dv)
+            rec(3)
+            sa.sa_bwd_dq(q, k, v, lse, do, lays, scale, ws, dq=dq)
+            rec(4)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    for s_ in range(args.steps):
+        step(events[s_])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_start
+    ms_per_step = wall * 1e3 / args.steps
+    kernel_ms = {nm: np.array([e[i].elapsed_time(e[i + 1]) for e in events]) for i, nm in enumerate(names)}
+
+    fwd_flops, blocks = counted_flops(lays, w.batch, T, d)
+    bwd_flops = 2.5 * fwd_flops if w.backward else 0.0
+    value = (fwd_flops + bwd_flops) / (ms_per_step * 1e-3) / 1e12
+    peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_F32_TFLOPS
+
+    # Counted (algorithmic) flops per launch, per listed block: forward 4*T*T*d;
+    # backward 10*T*T*d split as dK/dV 8*T*T*d (S, dP, dV, dK) and dQ 2*T*T*d
+    # (dQ itself; the S and dP it recomputes are not counted twice).
+    per_block = {"fwd": 4.0, "bwd_dkdv": 8.0, "bwd_dq": 2.0, "bwd_rowterms": 0.0}
+    kernels = {}
+    for nm in names:
+        avg_s = float(kernel_ms[nm].mean()) * 1e-3
+        fl = per_block[nm] * T * T * d * blocks
+        kernels[nm] = {"avg_us": avg_s * 1e6, "median_us": float(np.median(kernel_ms[nm])) * 1e3,
+                       "counted_gflop": fl / 1e9, "tflops": fl / avg_s / 1e12 if fl else None}
+    dominant = max(names, key=lambda nm: kernels[nm]["avg_us"])
+    kern_sym = {
+        "fwd": "fwd_bf16_t64_kernel<%d>" % d if w.dtype == "bf16" else "fwd_f32_t16_d64_kernel",
+        "bwd_rowterms": "bwd_delta_kernel<%d>" % d,
+        "bwd_dkdv": "bwd_dkdv_kernel<%d, %d>" % (d, 2 if d == 64 else 1),
+        "bwd_dq": "bwd_dq_kernel<%d, %d>" % (d, 2 if d == 64 else 1),
+    }
+    dk_ = kernels[dominant]
+    kern_file = "fwd.hip" if dominant == "fwd" else "bwd.hip"
+    roofline = {
+        "kernel": kern_sym[dominant],
+        "bound": "mfma",
+        "achieved": dk_["tflops"],
+        "peak": peak,
+        "unit": "TFLOP/s",
+        "frac": dk_["tflops"] / peak,
+        "traffic": traffic_from_profile(kern_file, kern_sym[dominant], w.name + ("-dense" if args.dense else "")),
+        "counted_flops_per_launch": dk_["counted_gflop"] * 1e9,
+        "avg_launch_us": dk_["avg_us"],
+    }
+    out = {
+        "metric": METRIC,
+        "value": value,
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic",
+        "config": {
+            "workload": w.name + ("-dense" if args.dense else ""),
+            "batch": w.batch, "heads": w.heads, "n": w.n, "head_dim": d, "block": T,
+            "pattern": "dense causal" if args.dense else w.pattern, "l": w.l, "c": w.c,
+            "scale": scale, "allowed_blocks": blocks, "backward": w.backward,
+        },
+        "frac_of_peak": value / peak,
+        "kernels": kernels,
+        "fwd_frac_of_peak": kernels["fwd"]["tflops"] / peak,
+        "layout_build_ms": layout_ms,
+        "roofline": roofline,
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        heads = args.cpu_heads or {"tiny": 2, "img32": 16, "text": 16, "img64": 24, "audio": 2}[w.name]
+        out["cpu_baseline"] = cpu_baseline(w, x, pats, T, heads)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

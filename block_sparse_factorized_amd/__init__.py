@@ -20,6 +20,9 @@ from ._binding import (  # noqa: F401
     SAError,
     library,
     sa_bwd,
+    sa_bwd_dkdv,
+    sa_bwd_dq,
+    sa_bwd_rowterms,
     sa_bwd_workspace_size,
     sa_fwd,
     sa_layout_build,

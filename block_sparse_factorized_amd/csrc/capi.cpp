@@ -331,31 +331,50 @@ size_t sa_bwd_workspace_size(int32_t B, int32_t H, int64_t n, int32_t d)
     return (((size_t)B * H * n * sizeof(float)) + 255) & ~(size_t)255;
 }
 
-int sa_bwd(const sa_layout_t* const* head_layout, int32_t B, int32_t H, int64_t n, int32_t d, int dtype, float scale,
-           const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dout, void* dq,
-           void* dk, void* dv, void* workspace, size_t ws_bytes, void* stream)
+}  // extern "C"
+
+namespace {
+
+enum BwdStage { kStageRowTerms = 1, kStageDkDv = 2, kStageDq = 4, kStageAll = 7 };
+
+int bwd_call(const char* fn, int stages, const sa_layout_t* const* head_layout, int32_t B, int32_t H, int64_t n,
+             int32_t d, int dtype, float scale, const void* q, const void* k, const void* v, const void* o,
+             const float* lse, const void* dout, void* dq, void* dk, void* dv, void* workspace, size_t ws_bytes,
+             void* stream)
 {
     HeadTable ht;
     int dev = 0, nl = 0;
     std::vector<sa_layout*> hl;
     sa_layout* distinct[kMaxLayouts];
-    int st = common_checks("sa_bwd", head_layout, B, H, n, d, dtype, scale, true, &ht, &hl, distinct, &nl);
+    int st = common_checks(fn, head_layout, B, H, n, d, dtype, scale, true, &ht, &hl, distinct, &nl);
     if (st != SA_OK) return st;
-    if (!q || !k || !v || !o || !lse || !dout || !dq || !dk || !dv || !workspace)
-        return fail(SA_ERR_INVALID_ARG, "sa_bwd: NULL pointer");
-    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(dout) || !aligned16(dq) ||
-        !aligned16(dk) || !aligned16(dv) || !aligned16(workspace) || ((uintptr_t)lse & 3))
-        return fail(SA_ERR_INVALID_ARG, "sa_bwd: tensors and workspace must be 16-byte aligned, lse 4-byte");
+    // Pointers each stage reads or writes.
+    const bool rt = stages & kStageRowTerms, kv = stages & kStageDkDv, dqs = stages & kStageDq;
+    std::vector<const void*> need = {workspace};
+    if (rt) need.insert(need.end(), {o, dout});
+    if (kv || dqs) need.insert(need.end(), {q, k, v, dout, (const void*)lse});
+    for (const void* p : need)
+        if (!p) return fail(SA_ERR_INVALID_ARG, "%s: NULL pointer", fn);
+    if ((kv && (!dk || !dv)) || (dqs && !dq)) return fail(SA_ERR_INVALID_ARG, "%s: NULL gradient pointer", fn);
+    const void* al16[] = {q, k, v, o, dout, dq, dk, dv, workspace};
+    for (const void* p : al16)
+        if (p && !aligned16(p))
+            return fail(SA_ERR_INVALID_ARG, "%s: tensors and workspace must be 16-byte aligned", fn);
+    if ((uintptr_t)lse & 3) return fail(SA_ERR_INVALID_ARG, "%s: lse must be 4-byte aligned", fn);
     if (ws_bytes < sa_bwd_workspace_size(B, H, n, d))
-        return fail(SA_ERR_INVALID_ARG, "sa_bwd: workspace of %zu bytes, %zu needed", ws_bytes,
+        return fail(SA_ERR_INVALID_ARG, "%s: workspace of %zu bytes, %zu needed", fn, ws_bytes,
                     sa_bwd_workspace_size(B, H, n, d));
     st = prepare_device(distinct, nl, &ht, &dev);
     if (st != SA_OK) return st;
-    Plan pk, pq;
-    st = get_plan(kByKey, dev, B, H, hl.data(), &pk);
-    if (st != SA_OK) return st;
-    st = get_plan(kByQuery, dev, B, H, hl.data(), &pq);
-    if (st != SA_OK) return st;
+    Plan pk{nullptr, 0}, pq{nullptr, 0};
+    if (kv) {
+        st = get_plan(kByKey, dev, B, H, hl.data(), &pk);
+        if (st != SA_OK) return st;
+    }
+    if (dqs) {
+        st = get_plan(kByQuery, dev, B, H, hl.data(), &pq);
+        if (st != SA_OK) return st;
+    }
     BwdArgs a;
     a.q = q;
     a.k = k;
@@ -373,17 +392,59 @@ int sa_bwd(const sa_layout_t* const* head_layout, int32_t B, int32_t H, int64_t 
     a.scale = scale;
     a.scale_log2 = scale * 1.4426950408889634f;
     a.heads = ht;
-    hipStream_t s = (hipStream_t)stream;
     a.items = nullptr;
-    hipError_t e = launch_bwd_delta_bf16(d, a, (int64_t)B * H * n, s);
-    if (e != hipSuccess) return hip_fail(e, "sa_bwd: delta kernel launch");
-    a.items = pk.items;
-    e = launch_bwd_dkdv_bf16_t64(d, a, pk.count, s);
-    if (e != hipSuccess) return hip_fail(e, "sa_bwd: dK/dV kernel launch");
-    a.items = pq.items;
-    e = launch_bwd_dq_bf16_t64(d, a, pq.count, s);
-    if (e != hipSuccess) return hip_fail(e, "sa_bwd: dQ kernel launch");
+    hipStream_t s = (hipStream_t)stream;
+    hipError_t e;
+    if (rt) {
+        e = launch_bwd_delta_bf16(d, a, (int64_t)B * H * n, s);
+        if (e != hipSuccess) return hip_fail(e, "sa_bwd: row-term kernel launch");
+    }
+    if (kv) {
+        a.items = pk.items;
+        e = launch_bwd_dkdv_bf16_t64(d, a, pk.count, s);
+        if (e != hipSuccess) return hip_fail(e, "sa_bwd: dK/dV kernel launch");
+    }
+    if (dqs) {
+        a.items = pq.items;
+        e = launch_bwd_dq_bf16_t64(d, a, pq.count, s);
+        if (e != hipSuccess) return hip_fail(e, "sa_bwd: dQ kernel launch");
+    }
     return SA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int sa_bwd(const sa_layout_t* const* head_layout, int32_t B, int32_t H, int64_t n, int32_t d, int dtype, float scale,
+           const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dout, void* dq,
+           void* dk, void* dv, void* workspace, size_t ws_bytes, void* stream)
+{
+    return bwd_call("sa_bwd", kStageAll, head_layout, B, H, n, d, dtype, scale, q, k, v, o, lse, dout, dq, dk, dv,
+                    workspace, ws_bytes, stream);
+}
+
+int sa_bwd_rowterms(const sa_layout_t* const* head_layout, int32_t B, int32_t H, int64_t n, int32_t d, int dtype,
+                    float scale, const void* o, const void* dout, void* workspace, size_t ws_bytes, void* stream)
+{
+    return bwd_call("sa_bwd_rowterms", kStageRowTerms, head_layout, B, H, n, d, dtype, scale, nullptr, nullptr,
+                    nullptr, o, nullptr, dout, nullptr, nullptr, nullptr, workspace, ws_bytes, stream);
+}
+
+int sa_bwd_dkdv(const sa_layout_t* const* head_layout, int32_t B, int32_t H, int64_t n, int32_t d, int dtype,
+                float scale, const void* q, const void* k, const void* v, const float* lse, const void* dout,
+                void* dk, void* dv, const void* workspace, size_t ws_bytes, void* stream)
+{
+    return bwd_call("sa_bwd_dkdv", kStageDkDv, head_layout, B, H, n, d, dtype, scale, q, k, v, nullptr, lse, dout,
+                    nullptr, dk, dv, const_cast<void*>(workspace), ws_bytes, stream);
+}
+
+int sa_bwd_dq(const sa_layout_t* const* head_layout, int32_t B, int32_t H, int64_t n, int32_t d, int dtype,
+              float scale, const void* q, const void* k, const void* v, const float* lse, const void* dout, void* dq,
+              const void* workspace, size_t ws_bytes, void* stream)
+{
+    return bwd_call("sa_bwd_dq", kStageDq, head_layout, B, H, n, d, dtype, scale, q, k, v, nullptr, lse, dout, dq,
+                    nullptr, nullptr, const_cast<void*>(workspace), ws_bytes, stream);
 }
 
 const char* sa_status_string(int status)

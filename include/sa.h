@@ -166,6 +166,30 @@ int sa_bwd(const sa_layout_t* const* head_layout, int32_t B, int32_t H, int64_t 
            const float* lse, const void* dout, void* dq, void* dk, void* dv, void* workspace,
            size_t ws_bytes, void* stream);
 
+/*
+ * The three stages of sa_bwd as separate calls, for callers that schedule
+ * them themselves (for instance dQ and dK/dV on two streams once the row
+ * terms are ready).  Arguments mean what they mean for sa_bwd; each call
+ * reads and writes only the pointers it takes.
+ *   sa_bwd_rowterms  D_i = sum_t dO_it O_it into the workspace
+ *   sa_bwd_dkdv      dK, dV (reads the row terms from the workspace), one
+ *                    workgroup per key block walking its query blocks
+ *   sa_bwd_dq        dQ (reads the row terms from the workspace), one
+ *                    workgroup per query block walking its key blocks
+ * sa_bwd_dkdv and sa_bwd_dq must be ordered after sa_bwd_rowterms on the
+ * device.  Same errors as sa_bwd.
+ */
+int sa_bwd_rowterms(const sa_layout_t* const* head_layout, int32_t B, int32_t H, int64_t n, int32_t d,
+                    int dtype, float scale, const void* o, const void* dout, void* workspace,
+                    size_t ws_bytes, void* stream);
+int sa_bwd_dkdv(const sa_layout_t* const* head_layout, int32_t B, int32_t H, int64_t n, int32_t d,
+                int dtype, float scale, const void* q, const void* k, const void* v, const float* lse,
+                const void* dout, void* dk, void* dv, const void* workspace, size_t ws_bytes,
+                void* stream);
+int sa_bwd_dq(const sa_layout_t* const* head_layout, int32_t B, int32_t H, int64_t n, int32_t d,
+              int dtype, float scale, const void* q, const void* k, const void* v, const float* lse,
+              const void* dout, void* dq, const void* workspace, size_t ws_bytes, void* stream);
+
 /* Static text of a status code. */
 const char* sa_status_string(int status);
 
