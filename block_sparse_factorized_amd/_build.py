@@ -17,8 +17,11 @@ LIB = os.path.join(OUT_DIR, "libsa.so")
 SOURCES = ["layout.cpp", "capi.cpp", "fwd.hip", "bwd.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
+# -amdgpu-mfma-vgpr-form: keep MFMA accumulators in ordinary VGPRs, so the
+# softmax's VALU work on them needs no accvgpr moves.
 FLAGS = ["--offload-arch=" + ARCH, "-O3", "-std=c++17", "-fPIC",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+         "-mllvm", "-amdgpu-mfma-vgpr-form=1",
          "-I" + os.path.join(os.path.dirname(HERE), "include")]
 
 

@@ -53,7 +53,10 @@ int device_layout(sa_layout* L, int dev, DevLayout* out)
     auto al = [](size_t x) { return (x + 255) & ~(size_t)255; };
     size_t off_masks = 0;
     size_t off_masks_t = al(off_masks + nwords * 8);
-    size_t off_row_ptr = al(off_masks_t + nwords * 8);
+    const size_t nplanes = L->T == 64 ? (size_t)L->n_masks * 64 : 0;
+    size_t off_planes = al(off_masks_t + nwords * 8);
+    size_t off_planes_t = al(off_planes + nplanes * 8);
+    size_t off_row_ptr = al(off_planes_t + nplanes * 8);
     size_t off_col_idx = al(off_row_ptr + nqb1 * 4);
     size_t off_mask_id = al(off_col_idx + nnz * 4);
     size_t off_col_ptr = al(off_mask_id + nnz * 4);
@@ -75,6 +78,28 @@ int device_layout(sa_layout* L, int dev, DevLayout* out)
                     if ((src[e >> 6] >> (e & 63)) & 1ull) dst[f >> 6] |= 1ull << (f & 63);
                 }
         }
+    }
+    if (nplanes) {
+        uint64_t* pl = (uint64_t*)&host[off_planes];
+        uint64_t* pt = (uint64_t*)&host[off_planes_t];
+        auto bit = [&](int64_t m, int r, int s2) {
+            int64_t e = (int64_t)r * 64 + s2;
+            return (L->masks[m * 64 + (e >> 6)] >> (e & 63)) & 1ull;
+        };
+        for (int64_t m = 0; m < L->n_masks; ++m)
+            for (int w = 0; w < 2; ++w)
+                for (int reg = 0; reg < 32; ++reg) {
+                    const int t = reg / 16, i = reg % 16;
+                    uint64_t a = 0, b = 0;
+                    for (int lane = 0; lane < 64; ++lane) {
+                        const int inner = 32 * t + 8 * (i / 4) + 4 * (lane / 32) + i % 4;
+                        const int outer = 32 * w + lane % 32;
+                        a |= bit(m, outer, inner) << lane;
+                        b |= bit(m, inner, outer) << lane;
+                    }
+                    pl[(m * 2 + w) * 32 + reg] = a;
+                    pt[(m * 2 + w) * 32 + reg] = b;
+                }
     }
     memcpy(&host[off_row_ptr], L->row_ptr.data(), nqb1 * 4);
     if (nnz) {
@@ -98,6 +123,8 @@ int device_layout(sa_layout* L, int dev, DevLayout* out)
     DevLayout v;
     v.masks = (const uint64_t*)(b + off_masks);
     v.masks_t = (const uint64_t*)(b + off_masks_t);
+    v.planes = nplanes ? (const uint64_t*)(b + off_planes) : nullptr;
+    v.planes_t = nplanes ? (const uint64_t*)(b + off_planes_t) : nullptr;
     v.row_ptr = (const int32_t*)(b + off_row_ptr);
     v.col_idx = (const int32_t*)(b + off_col_idx);
     v.mask_id = (const int32_t*)(b + off_mask_id);

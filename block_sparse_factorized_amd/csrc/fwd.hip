@@ -42,33 +42,84 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 
-constexpr float kLog2e = 1.4426950408889634f;
-
-__device__ inline int swap_bits23(int x) { return (x & ~12) | ((x & 4) << 1) | ((x & 8) >> 1); }
-
-__device__ inline unsigned pack_lo(unsigned a, unsigned b) { return (a & 0xffffu) | (b << 16); }
-__device__ inline unsigned pack_hi(unsigned a, unsigned b) { return (a >> 16) | (b & 0xffff0000u); }
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(1))) void glb_void;
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(4))) const uint64_t const_u64;
+typedef __attribute__((address_space(4))) const int32_t const_i32;
 
 __device__ inline unsigned bf16_pair(float x, float y)
 {
-    __bf16 a = (__bf16)x, b = (__bf16)y;
-    unsigned short ua = __builtin_bit_cast(unsigned short, a);
-    unsigned short ub = __builtin_bit_cast(unsigned short, b);
-    return (unsigned)ua | ((unsigned)ub << 16);
+    return __builtin_bit_cast(unsigned, __builtin_convertvector((f32x2){x, y}, bf16x2));
 }
+
+// Registers first..first+7 of x as eight bf16 (round to nearest even).
+__device__ inline bf16x8 pack8(const f32x16& x, int first)
+{
+    u32x4 u;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) u[e] = bf16_pair(x[first + 2 * e], x[first + 2 * e + 1]);
+    return __builtin_bit_cast(bf16x8, u);
+}
+
+// Max of x over lanes n and n+32 (lane pairs that hold the same query row).
+__device__ inline float half_max(float x)
+{
+    auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __builtin_fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
+// The value lane n+32 (or n-32) holds.
+__device__ inline float swap_halves(float x)
+{
+    auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float((__lane_id() < 32) ? r[1] : r[0]);
+}
+
+__device__ inline void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }  // vmcnt(0)
+
+// Two transposing 8-byte LDS reads (ds_read_b64_tr_b16) forming one 8 x bf16 operand.
+__device__ inline bf16x8 lds_read_tr8(const unsigned char* p0, const unsigned char* p1)
+{
+    i16x4 x = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)(lds_void*)p0);
+    i16x4 y = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)(lds_void*)p1);
+    return __builtin_bit_cast(bf16x8, __builtin_shufflevector(x, y, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
+// A 64 x D bf16 tile in LDS: rows unpadded (2*D bytes), each row's 16-byte
+// chunks stored at position chunk ^ swz(row), which spreads the rows that
+// one MFMA operand read touches over all LDS banks.  Filled by direct
+// global-to-LDS loads: load u of wave w writes 1 KB of consecutive slots,
+// lane l the 16 bytes at slot l.
+template <int D>
+struct Tile64 {
+    static constexpr int kRow = 2 * D;
+    static constexpr int kBytes = 64 * kRow;
+    __device__ static inline int swz(int r) { return D == 64 ? ((r >> 1) & 7) : (r & 15); }
+    __device__ static inline int off(int r, int chunk) { return r * kRow + ((chunk ^ swz(r)) << 4); }
+    __device__ static inline int load_dst(int u, int w) { return (2 * u + w) * 1024; }
+    // Element offset in the global tile of the 16 bytes lane `lane` loads in load u of wave w.
+    __device__ static inline int load_src(int u, int w, int lane)
+    {
+        const int byte = load_dst(u, w) + 16 * lane;
+        const int r = byte / kRow, pos = (byte % kRow) >> 4;
+        return r * D + ((pos ^ swz(r)) << 3);
+    }
+};
 
 template <int D>
 __global__ __launch_bounds__(128) void fwd_bf16_t64_kernel(const FwdArgs a)
 {
     constexpr int T = 64;
-    constexpr int KP = D + 8;  // K tile row pitch (elements)
-    constexpr int VP = T + 8;  // V^T tile row pitch (elements)
-    constexpr int KCH = T * D / 8 / 128;          // 16-byte K chunks per thread
-    constexpr int VBL = (T / 4) * (D / 8) / 128;  // 4x8 V blocks per thread
-    __shared__ __attribute__((aligned(16))) unsigned short ks[2][T * KP];
-    __shared__ __attribute__((aligned(16))) unsigned short vts[2][D * VP];
+    typedef Tile64<D> TL;
+    constexpr int NI = TL::kBytes / 2048;  // direct-to-LDS loads per wave per tensor
+    __shared__ __attribute__((aligned(1024))) unsigned char kbuf0[TL::kBytes], kbuf1[TL::kBytes];
+    __shared__ __attribute__((aligned(1024))) unsigned char vbuf0[TL::kBytes], vbuf1[TL::kBytes];
 
-    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int n32 = lane & 31, hh = lane >> 5;
     const Item item = a.items[blockIdx.x];
     const int bh = item.bh, qb = item.blk;
@@ -80,9 +131,31 @@ __global__ __launch_bounds__(128) void fwd_bf16_t64_kernel(const FwdArgs a)
     const int q_local = 32 * w + n32;
     const int64_t q_row = (int64_t)qb * T + q_local;
 
+    // Q^T as the B operand of S^T = K Q^T: lane (hh, n) holds d = 16c + 8hh .. +7 of query n.
     bf16x8 qop[D / 16];
 #pragma unroll
     for (int c = 0; c < D / 16; ++c) qop[c] = *(const bf16x8*)(Q + q_row * D + 16 * c + 8 * hh);
+
+    // Per-thread element offsets of the direct-to-LDS loads (the same for every tile).
+    int goff[NI];
+#pragma unroll
+    for (int u = 0; u < NI; ++u) goff[u] = TL::load_src(u, w, lane);
+    // LDS byte offsets of this lane's K reads (A operand of S^T) and V transposing reads.
+    int koff[D / 16];
+#pragma unroll
+    for (int c = 0; c < D / 16; ++c) koff[c] = TL::off(n32, 2 * c + hh);
+    int voff[2][D / 32];
+    {
+        const int g = lane >> 4, vh = g >> 1, dh = g & 1, al = lane & 15;
+#pragma unroll
+        for (int j4 = 0; j4 < 2; ++j4)
+#pragma unroll
+            for (int dt = 0; dt < D / 32; ++dt) {
+                const int row = 8 * j4 + 4 * vh + (al >> 2);
+                const int col = 32 * dt + 16 * dh + 4 * (al & 3);
+                voff[j4][dt] = TL::off(row, col >> 3) + ((col & 4) << 1);
+            }
+    }
 
     const int p0 = L.row_ptr[qb];
     const int nblk = L.row_ptr[qb + 1] - p0;
@@ -92,61 +165,31 @@ __global__ __launch_bounds__(128) void fwd_bf16_t64_kernel(const FwdArgs a)
     for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
         for (int i = 0; i < 16; ++i) oacc[dt][i] = 0.f;
-    float m_run = -INFINITY, l_run = 0.f;
+    float m_ref = -INFINITY, l_run = 0.f;
     const float c2 = a.scale_log2;
 
-    u32x4 kreg[KCH];
-    u32x4 vreg[VBL][4];
-    auto gload = [&](int kb) {
+    auto issue = [&](int kb, unsigned char* kd, unsigned char* vd) {
         const unsigned short* Kt = K + (int64_t)kb * T * D;
         const unsigned short* Vt = V + (int64_t)kb * T * D;
 #pragma unroll
-        for (int u = 0; u < KCH; ++u) {
-            int idx = tid + 128 * u, row = idx / (D / 8), c8 = idx % (D / 8);
-            kreg[u] = *(const u32x4*)(Kt + row * D + c8 * 8);
-        }
-#pragma unroll
-        for (int b = 0; b < VBL; ++b) {
-            int idx = tid + 128 * b, kg = idx / (D / 8), dc = idx % (D / 8);
-#pragma unroll
-            for (int r = 0; r < 4; ++r) vreg[b][r] = *(const u32x4*)(Vt + (4 * kg + r) * D + dc * 8);
-        }
-    };
-    auto sstore = [&](int buf) {
-#pragma unroll
-        for (int u = 0; u < KCH; ++u) {
-            int idx = tid + 128 * u, row = idx / (D / 8), c8 = idx % (D / 8);
-            *(u32x4*)&ks[buf][row * KP + c8 * 8] = kreg[u];
-        }
-#pragma unroll
-        for (int b = 0; b < VBL; ++b) {
-            int idx = tid + 128 * b, kg = idx / (D / 8), dc = idx % (D / 8);
-            int pos = swap_bits23(4 * kg);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                u32x2 lo, hi;
-                lo[0] = pack_lo(vreg[b][0][e], vreg[b][1][e]);
-                lo[1] = pack_lo(vreg[b][2][e], vreg[b][3][e]);
-                hi[0] = pack_hi(vreg[b][0][e], vreg[b][1][e]);
-                hi[1] = pack_hi(vreg[b][2][e], vreg[b][3][e]);
-                *(u32x2*)&vts[buf][(dc * 8 + 2 * e) * VP + pos] = lo;
-                *(u32x2*)&vts[buf][(dc * 8 + 2 * e + 1) * VP + pos] = hi;
-            }
+        for (int u = 0; u < NI; ++u) {
+            __builtin_amdgcn_global_load_lds((glb_void*)(Kt + goff[u]), (lds_void*)(kd + TL::load_dst(u, w)), 16, 0, 0);
+            __builtin_amdgcn_global_load_lds((glb_void*)(Vt + goff[u]), (lds_void*)(vd + TL::load_dst(u, w)), 16, 0, 0);
         }
     };
 
-    if (nblk > 0) {
-        gload(L.col_idx[p0]);
-        sstore(0);
-    }
+    if (nblk > 0) issue(L.col_idx[p0], kbuf0, vbuf0);
+    wait_vmem();
     __syncthreads();
 
     for (int t = 0; t < nblk; ++t) {
-        const int buf = t & 1;
-        if (t + 1 < nblk) gload(L.col_idx[p0 + t + 1]);
+        const bool odd = t & 1;
+        const unsigned char* kc = odd ? kbuf1 : kbuf0;
+        const unsigned char* vc = odd ? vbuf1 : vbuf0;
+        if (t + 1 < nblk) issue(L.col_idx[p0 + t + 1], odd ? kbuf0 : kbuf1, odd ? vbuf0 : vbuf1);
         const int mid = L.mask_id[p0 + t];
 
-        // S^T = K Q^T for keys 0-31 (kt = 0) and 32-63 (kt = 1).
+        // S^T = K Q^T: register i of s[kt] holds key 32*kt + 8*(i/4) + 4*hh + i%4 of query n.
         f32x16 s[2];
 #pragma unroll
         for (int kt = 0; kt < 2; ++kt) {
@@ -154,72 +197,69 @@ __global__ __launch_bounds__(128) void fwd_bf16_t64_kernel(const FwdArgs a)
             for (int i = 0; i < 16; ++i) s[kt][i] = 0.f;
 #pragma unroll
             for (int c = 0; c < D / 16; ++c) {
-                bf16x8 kop = *(const bf16x8*)&ks[buf][(32 * kt + n32) * KP + 16 * c + 8 * hh];
+                const bf16x8 kop = *(const bf16x8*)(kc + koff[c] + kt * 32 * TL::kRow);
                 s[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop, qop[c], s[kt], 0, 0, 0);
             }
         }
-        // Register i of tile kt holds key 32*kt + 8*(i/4) + 4*hh + i%4.
+        // Partial block: lane masks of every register, one 64-bit plane each, in SGPRs.
         if (mid >= 0) {
-            uint64_t word = L.masks[(int64_t)mid * (T * T / 64) + q_local] >> (4 * hh);
-            unsigned wl = (unsigned)word, wh = (unsigned)(word >> 32);
+            // Read-only for the kernel's lifetime: the constant address space
+            // lets these wave-uniform loads go to SGPRs (s_load_dwordx16).
+            const_u64* pl = (const_u64*)(L.planes + ((int64_t)mid * 2 + w) * 32);
 #pragma unroll
-            for (int kt = 0; kt < 2; ++kt) {
-                unsigned bits = kt ? wh : wl;
+            for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
                 for (int i = 0; i < 16; ++i)
-                    if (!((bits >> (8 * (i / 4) + (i % 4))) & 1u)) s[kt][i] = -INFINITY;
-            }
+                    s[kt][i] = __builtin_amdgcn_inverse_ballot_w64(pl[16 * kt + i]) ? s[kt][i] : -INFINITY;
         }
-        float mx = -INFINITY;
+        float mx = s[0][0];
 #pragma unroll
-        for (int kt = 0; kt < 2; ++kt)
+        for (int i = 1; i < 16; ++i) mx = __builtin_fmaxf(mx, s[0][i]);
 #pragma unroll
-            for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[kt][i]);
-        mx = fmaxf(mx, __shfl_xor(mx, 32));
-        const float m_new = fmaxf(m_run, mx);
-        const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-        const float alpha = __builtin_amdgcn_exp2f((m_run - m_use) * c2);
-        const float mc = m_use * c2;
+        for (int i = 0; i < 16; ++i) mx = __builtin_fmaxf(mx, s[1][i]);
+        mx = half_max(mx);
+
+        // Lazy rescale: keep the reference max unless some row's max grew by more
+        // than 2^8 in the exponent (then every lane of the wave rescales).
+        const float m_new = __builtin_fmaxf(m_ref, mx);
+        if (__builtin_amdgcn_ballot_w64((m_new - m_ref) * c2 > 8.f)) {
+            const float alpha = m_new == -INFINITY ? 1.f : __builtin_amdgcn_exp2f((m_ref - m_new) * c2);
+            l_run *= alpha;
+#pragma unroll
+            for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+                for (int i = 0; i < 16; ++i) oacc[dt][i] *= alpha;
+            m_ref = m_new;
+        }
+        const float mc = m_ref == -INFINITY ? 0.f : m_ref * c2;
         float lsum = 0.f;
 #pragma unroll
         for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
             for (int i = 0; i < 16; ++i) {
-                float p = __builtin_amdgcn_exp2f(fmaf(s[kt][i], c2, -mc));
+                const float p = __builtin_amdgcn_exp2f(fmaf(s[kt][i], c2, -mc));
                 s[kt][i] = p;
                 lsum += p;
             }
-        l_run = l_run * alpha + lsum;
-        m_run = m_new;
-#pragma unroll
-        for (int dt = 0; dt < D / 32; ++dt)
-#pragma unroll
-            for (int i = 0; i < 16; ++i) oacc[dt][i] *= alpha;
+        l_run += lsum;
 
-        // P^T as the B operand: chunk cc holds registers 8*(cc%2)..+7 of tile cc/2.
-        bf16x8 pb[4];
+        // O^T += V^T P^T; chunk cc of P^T is registers 8*(cc%2)..+7 of s[cc/2].
 #pragma unroll
         for (int cc = 0; cc < 4; ++cc) {
-            u32x4 u;
+            const bf16x8 pb = pack8(s[cc / 2], 8 * (cc % 2));
 #pragma unroll
-            for (int e = 0; e < 4; ++e)
-                u[e] = bf16_pair(s[cc / 2][8 * (cc % 2) + 2 * e], s[cc / 2][8 * (cc % 2) + 2 * e + 1]);
-            pb[cc] = __builtin_bit_cast(bf16x8, u);
-        }
-        // O^T += V^T P^T.
-#pragma unroll
-        for (int dt = 0; dt < D / 32; ++dt)
-#pragma unroll
-            for (int cc = 0; cc < 4; ++cc) {
-                bf16x8 vop = *(const bf16x8*)&vts[buf][(32 * dt + n32) * VP + 16 * cc + 8 * hh];
-                oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop, pb[cc], oacc[dt], 0, 0, 0);
+            for (int dt = 0; dt < D / 32; ++dt) {
+                const bf16x8 vop = lds_read_tr8(vc + voff[0][dt] + cc * 16 * TL::kRow,
+                                                vc + voff[1][dt] + cc * 16 * TL::kRow);
+                oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop, pb, oacc[dt], 0, 0, 0);
             }
+        }
 
-        if (t + 1 < nblk) sstore(buf ^ 1);
+        wait_vmem();
         __syncthreads();
     }
 
-    const float l_tot = l_run + __shfl_xor(l_run, 32);
+    const float l_tot = l_run + swap_halves(l_run);
     const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
     unsigned short* O = (unsigned short*)a.o + head + q_row * D;
     // Register i of oacc[dt] holds d = 32*dt + 8*(i/4) + 4*hh + i%4 of query q_row.
@@ -233,7 +273,7 @@ __global__ __launch_bounds__(128) void fwd_bf16_t64_kernel(const FwdArgs a)
             *(u32x2*)(O + 32 * dt + 8 * g + 4 * hh) = u;
         }
     if (hh == 0)
-        a.lse[(int64_t)bh * a.n + q_row] = l_tot > 0.f ? m_run * a.scale + logf(l_tot) : -INFINITY;
+        a.lse[(int64_t)bh * a.n + q_row] = l_tot > 0.f ? m_ref * a.scale + logf(l_tot) : -INFINITY;
 }
 
 __global__ __launch_bounds__(64) void fwd_f32_t16_d64_kernel(const FwdArgs a)

@@ -23,6 +23,14 @@ struct DevLayout {
     const uint64_t* masks;    // [n_masks][T*T/64]  element (r, s): bit r*T+s
     const uint64_t* masks_t;  // [n_masks][T*T/64]  the same masks transposed:
                               //                    element (r, s): bit s*T+r
+    // Block size 64 only: the masks as 64-bit lane masks ("planes") of the
+    // 32x32 MFMA accumulator layout, [n_masks][wave w = 0, 1][register 0..31].
+    //   planes:   bit L of register 16*t + i = element (row 32w + L%32,
+    //             key 32t + 8(i/4) + 4(L/32) + i%4)   (lane = query row)
+    //   planes_t: bit L of register 16*t + i = element (row 32t + 8(i/4) +
+    //             4(L/32) + i%4, key 32w + L%32)       (lane = key column)
+    const uint64_t* planes;
+    const uint64_t* planes_t;
     const int32_t* col_ptr;   // [nqb+1]   listing by key block
     const int32_t* row_idx;   // [nnz]     query blocks, ascending per key block
     const int32_t* col_mask;  // [nnz]     mask id of each transposed entry
