@@ -164,11 +164,11 @@ def main():
         sa.sa_fwd(q, k, v, lays, scale, o=o, lse=lse)
         rec(1)
         if w.backward:
-            sa.sa_bwd_rowterms(o, do, lays, scale, workspace=ws)
+            sa.sa_bwd_rowterms(o, lse, do, lays, scale, workspace=ws)
             rec(2)
-            sa.sa_bwd_dkdv(q, k, v, lse, do, lays, scale, ws, dk=dk, dv=dv)
+            sa.sa_bwd_dkdv(q, k, v, do, lays, scale, ws, dk=dk, dv=dv)
             rec(3)
-            sa.sa_bwd_dq(q, k, v, lse, do, lays, scale, ws, dq=dq)
+            sa.sa_bwd_dq(q, k, v, do, lays, scale, ws, dq=dq)
             rec(4)
 
     for _ in range(args.warmup):
@@ -203,9 +203,9 @@ def main():
     dominant = max(names, key=lambda nm: kernels[nm]["avg_us"])
     kern_sym = {
         "fwd": "fwd_bf16_t64_kernel<%d>" % d if w.dtype == "bf16" else "fwd_f32_t16_d64_kernel",
-        "bwd_rowterms": "bwd_delta_kernel<%d>" % d,
-        "bwd_dkdv": "bwd_dkdv_kernel<%d, %d>" % (d, 2 if d == 64 else 1),
-        "bwd_dq": "bwd_dq_kernel<%d, %d>" % (d, 2 if d == 64 else 1),
+        "bwd_rowterms": "bwd_rowterms_kernel<%d>" % d,
+        "bwd_dkdv": "bwd_dkdv_kernel<%d>" % d,
+        "bwd_dq": "bwd_dq_kernel<%d>" % d,
     }
     dk_ = kernels[dominant]
     kern_file = "fwd.hip" if dominant == "fwd" else "bwd.hip"

@@ -66,11 +66,11 @@ def _load():
     lib.sa_bwd_workspace_size.restype = sz
     lib.sa_bwd.argtypes = [vp, i32, i32, i64, i32, cint, flt] + [vp] * 10 + [sz, vp]
     lib.sa_bwd.restype = cint
-    lib.sa_bwd_rowterms.argtypes = [vp, i32, i32, i64, i32, cint, flt, vp, vp, vp, sz, vp]
+    lib.sa_bwd_rowterms.argtypes = [vp, i32, i32, i64, i32, cint, flt, vp, vp, vp, vp, sz, vp]
     lib.sa_bwd_rowterms.restype = cint
-    lib.sa_bwd_dkdv.argtypes = [vp, i32, i32, i64, i32, cint, flt] + [vp] * 8 + [sz, vp]
+    lib.sa_bwd_dkdv.argtypes = [vp, i32, i32, i64, i32, cint, flt] + [vp] * 7 + [sz, vp]
     lib.sa_bwd_dkdv.restype = cint
-    lib.sa_bwd_dq.argtypes = [vp, i32, i32, i64, i32, cint, flt] + [vp] * 7 + [sz, vp]
+    lib.sa_bwd_dq.argtypes = [vp, i32, i32, i64, i32, cint, flt] + [vp] * 6 + [sz, vp]
     lib.sa_bwd_dq.restype = cint
     lib.sa_status_string.argtypes = [cint]
     lib.sa_status_string.restype = ctypes.c_char_p
@@ -243,43 +243,44 @@ def _bwd_common(q, layouts, workspace):
     return B, H, n, d, _head_array(layouts, H), workspace
 
 
-def sa_bwd_rowterms(o, do, layouts, scale: float, workspace=None, stream=None):
-    """Stage 1 of the backward: D_i = sum_t dO_it O_it into ``workspace``
-    (allocated and returned when None)."""
+def sa_bwd_rowterms(o, lse, do, layouts, scale: float, workspace=None, stream=None):
+    """Stage 1 of the backward: the row terms D_i = sum_t dO_it O_it and
+    -lse_i log2(e) into ``workspace`` (allocated and returned when None)."""
+    import torch
     _check_tensor("do", do, o.shape, o.dtype, o.device)
     B, H, n, d, heads, workspace = _bwd_common(o, layouts, workspace)
-    _check(_lib.sa_bwd_rowterms(heads, B, H, n, d, _dtype_code(o), float(scale), o.data_ptr(), do.data_ptr(),
-                                workspace.data_ptr(), workspace.numel(), _stream_handle(stream, o.device)))
+    _check_tensor("lse", lse, (B, H, n), torch.float32, o.device)
+    _check(_lib.sa_bwd_rowterms(heads, B, H, n, d, _dtype_code(o), float(scale), o.data_ptr(), lse.data_ptr(),
+                                do.data_ptr(), workspace.data_ptr(), workspace.numel(),
+                                _stream_handle(stream, o.device)))
     return workspace
 
 
-def sa_bwd_dkdv(q, k, v, lse, do, layouts, scale: float, workspace, dk=None, dv=None, stream=None):
+def sa_bwd_dkdv(q, k, v, do, layouts, scale: float, workspace, dk=None, dv=None, stream=None):
     """Stage 2: dK, dV (needs the row terms in ``workspace``)."""
     import torch
     for name, t in (("k", k), ("v", v), ("do", do)):
         _check_tensor(name, t, q.shape, q.dtype, q.device)
     B, H, n, d, heads, workspace = _bwd_common(q, layouts, workspace)
-    _check_tensor("lse", lse, (B, H, n), torch.float32, q.device)
     dk = torch.empty_like(q) if dk is None else dk
     dv = torch.empty_like(q) if dv is None else dv
     for name, t in (("dk", dk), ("dv", dv)):
         _check_tensor(name, t, q.shape, q.dtype, q.device)
     _check(_lib.sa_bwd_dkdv(heads, B, H, n, d, _dtype_code(q), float(scale), q.data_ptr(), k.data_ptr(),
-                            v.data_ptr(), lse.data_ptr(), do.data_ptr(), dk.data_ptr(), dv.data_ptr(),
+                            v.data_ptr(), do.data_ptr(), dk.data_ptr(), dv.data_ptr(),
                             workspace.data_ptr(), workspace.numel(), _stream_handle(stream, q.device)))
     return dk, dv
 
 
-def sa_bwd_dq(q, k, v, lse, do, layouts, scale: float, workspace, dq=None, stream=None):
+def sa_bwd_dq(q, k, v, do, layouts, scale: float, workspace, dq=None, stream=None):
     """Stage 3: dQ (needs the row terms in ``workspace``)."""
     import torch
     for name, t in (("k", k), ("v", v), ("do", do)):
         _check_tensor(name, t, q.shape, q.dtype, q.device)
     B, H, n, d, heads, workspace = _bwd_common(q, layouts, workspace)
-    _check_tensor("lse", lse, (B, H, n), torch.float32, q.device)
     dq = torch.empty_like(q) if dq is None else dq
     _check_tensor("dq", dq, q.shape, q.dtype, q.device)
     _check(_lib.sa_bwd_dq(heads, B, H, n, d, _dtype_code(q), float(scale), q.data_ptr(), k.data_ptr(),
-                          v.data_ptr(), lse.data_ptr(), do.data_ptr(), dq.data_ptr(), workspace.data_ptr(),
+                          v.data_ptr(), do.data_ptr(), dq.data_ptr(), workspace.data_ptr(),
                           workspace.numel(), _stream_handle(stream, q.device)))
     return dq

@@ -355,7 +355,7 @@ size_t sa_bwd_workspace_size(int32_t B, int32_t H, int64_t n, int32_t d)
 {
     (void)d;
     if (B < 1 || H < 1 || n < 1) return 0;
-    return (((size_t)B * H * n * sizeof(float)) + 255) & ~(size_t)255;
+    return ((2 * (size_t)B * H * n * sizeof(float)) + 255) & ~(size_t)255;
 }
 
 }  // extern "C"
@@ -378,8 +378,8 @@ int bwd_call(const char* fn, int stages, const sa_layout_t* const* head_layout, 
     // Pointers each stage reads or writes.
     const bool rt = stages & kStageRowTerms, kv = stages & kStageDkDv, dqs = stages & kStageDq;
     std::vector<const void*> need = {workspace};
-    if (rt) need.insert(need.end(), {o, dout});
-    if (kv || dqs) need.insert(need.end(), {q, k, v, dout, (const void*)lse});
+    if (rt) need.insert(need.end(), {o, dout, (const void*)lse});
+    if (kv || dqs) need.insert(need.end(), {q, k, v, dout});
     for (const void* p : need)
         if (!p) return fail(SA_ERR_INVALID_ARG, "%s: NULL pointer", fn);
     if ((kv && (!dk || !dv)) || (dqs && !dq)) return fail(SA_ERR_INVALID_ARG, "%s: NULL gradient pointer", fn);
@@ -413,6 +413,7 @@ int bwd_call(const char* fn, int stages, const sa_layout_t* const* head_layout, 
     a.dk = dk;
     a.dv = dv;
     a.delta = (float*)workspace;
+    a.nl2 = (float*)workspace + (size_t)B * H * n;
     a.n = n;
     a.H = H;
     a.BH = B * H;
@@ -423,7 +424,7 @@ int bwd_call(const char* fn, int stages, const sa_layout_t* const* head_layout, 
     hipStream_t s = (hipStream_t)stream;
     hipError_t e;
     if (rt) {
-        e = launch_bwd_delta_bf16(d, a, (int64_t)B * H * n, s);
+        e = launch_bwd_rowterms_bf16(d, a, (int64_t)B * H * n, s);
         if (e != hipSuccess) return hip_fail(e, "sa_bwd: row-term kernel launch");
     }
     if (kv) {
@@ -452,25 +453,26 @@ int sa_bwd(const sa_layout_t* const* head_layout, int32_t B, int32_t H, int64_t 
 }
 
 int sa_bwd_rowterms(const sa_layout_t* const* head_layout, int32_t B, int32_t H, int64_t n, int32_t d, int dtype,
-                    float scale, const void* o, const void* dout, void* workspace, size_t ws_bytes, void* stream)
+                    float scale, const void* o, const float* lse, const void* dout, void* workspace, size_t ws_bytes,
+                    void* stream)
 {
     return bwd_call("sa_bwd_rowterms", kStageRowTerms, head_layout, B, H, n, d, dtype, scale, nullptr, nullptr,
-                    nullptr, o, nullptr, dout, nullptr, nullptr, nullptr, workspace, ws_bytes, stream);
+                    nullptr, o, lse, dout, nullptr, nullptr, nullptr, workspace, ws_bytes, stream);
 }
 
 int sa_bwd_dkdv(const sa_layout_t* const* head_layout, int32_t B, int32_t H, int64_t n, int32_t d, int dtype,
-                float scale, const void* q, const void* k, const void* v, const float* lse, const void* dout,
-                void* dk, void* dv, const void* workspace, size_t ws_bytes, void* stream)
+                float scale, const void* q, const void* k, const void* v, const void* dout, void* dk, void* dv,
+                const void* workspace, size_t ws_bytes, void* stream)
 {
-    return bwd_call("sa_bwd_dkdv", kStageDkDv, head_layout, B, H, n, d, dtype, scale, q, k, v, nullptr, lse, dout,
+    return bwd_call("sa_bwd_dkdv", kStageDkDv, head_layout, B, H, n, d, dtype, scale, q, k, v, nullptr, nullptr, dout,
                     nullptr, dk, dv, const_cast<void*>(workspace), ws_bytes, stream);
 }
 
 int sa_bwd_dq(const sa_layout_t* const* head_layout, int32_t B, int32_t H, int64_t n, int32_t d, int dtype,
-              float scale, const void* q, const void* k, const void* v, const float* lse, const void* dout, void* dq,
+              float scale, const void* q, const void* k, const void* v, const void* dout, void* dq,
               const void* workspace, size_t ws_bytes, void* stream)
 {
-    return bwd_call("sa_bwd_dq", kStageDq, head_layout, B, H, n, d, dtype, scale, q, k, v, nullptr, lse, dout, dq,
+    return bwd_call("sa_bwd_dq", kStageDq, head_layout, B, H, n, d, dtype, scale, q, k, v, nullptr, nullptr, dout, dq,
                     nullptr, nullptr, const_cast<void*>(workspace), ws_bytes, stream);
 }
 

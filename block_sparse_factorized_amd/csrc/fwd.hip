@@ -32,82 +32,10 @@
 #include <hip/hip_runtime.h>
 
 #include "kernel_args.h"
+#include "tiles.h"
 
 namespace sa {
 namespace {
-
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef float f32x16 __attribute__((ext_vector_type(16)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
-typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
-
-typedef __attribute__((address_space(3))) void lds_void;
-typedef __attribute__((address_space(1))) void glb_void;
-typedef float f32x2 __attribute__((ext_vector_type(2)));
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-typedef short i16x4 __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(4))) const uint64_t const_u64;
-typedef __attribute__((address_space(4))) const int32_t const_i32;
-
-__device__ inline unsigned bf16_pair(float x, float y)
-{
-    return __builtin_bit_cast(unsigned, __builtin_convertvector((f32x2){x, y}, bf16x2));
-}
-
-// Registers first..first+7 of x as eight bf16 (round to nearest even).
-__device__ inline bf16x8 pack8(const f32x16& x, int first)
-{
-    u32x4 u;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) u[e] = bf16_pair(x[first + 2 * e], x[first + 2 * e + 1]);
-    return __builtin_bit_cast(bf16x8, u);
-}
-
-// Max of x over lanes n and n+32 (lane pairs that hold the same query row).
-__device__ inline float half_max(float x)
-{
-    auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-    return __builtin_fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
-}
-
-// The value lane n+32 (or n-32) holds.
-__device__ inline float swap_halves(float x)
-{
-    auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-    return __uint_as_float((__lane_id() < 32) ? r[1] : r[0]);
-}
-
-__device__ inline void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }  // vmcnt(0)
-
-// Two transposing 8-byte LDS reads (ds_read_b64_tr_b16) forming one 8 x bf16 operand.
-__device__ inline bf16x8 lds_read_tr8(const unsigned char* p0, const unsigned char* p1)
-{
-    i16x4 x = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)(lds_void*)p0);
-    i16x4 y = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)(lds_void*)p1);
-    return __builtin_bit_cast(bf16x8, __builtin_shufflevector(x, y, 0, 1, 2, 3, 4, 5, 6, 7));
-}
-
-// A 64 x D bf16 tile in LDS: rows unpadded (2*D bytes), each row's 16-byte
-// chunks stored at position chunk ^ swz(row), which spreads the rows that
-// one MFMA operand read touches over all LDS banks.  Filled by direct
-// global-to-LDS loads: load u of wave w writes 1 KB of consecutive slots,
-// lane l the 16 bytes at slot l.
-template <int D>
-struct Tile64 {
-    static constexpr int kRow = 2 * D;
-    static constexpr int kBytes = 64 * kRow;
-    __device__ static inline int swz(int r) { return D == 64 ? ((r >> 1) & 7) : (r & 15); }
-    __device__ static inline int off(int r, int chunk) { return r * kRow + ((chunk ^ swz(r)) << 4); }
-    __device__ static inline int load_dst(int u, int w) { return (2 * u + w) * 1024; }
-    // Element offset in the global tile of the 16 bytes lane `lane` loads in load u of wave w.
-    __device__ static inline int load_src(int u, int w, int lane)
-    {
-        const int byte = load_dst(u, w) + 16 * lane;
-        const int r = byte / kRow, pos = (byte % kRow) >> 4;
-        return r * D + ((pos ^ swz(r)) << 3);
-    }
-};
 
 template <int D>
 __global__ __launch_bounds__(128) void fwd_bf16_t64_kernel(const FwdArgs a)
@@ -145,17 +73,10 @@ __global__ __launch_bounds__(128) void fwd_bf16_t64_kernel(const FwdArgs a)
 #pragma unroll
     for (int c = 0; c < D / 16; ++c) koff[c] = TL::off(n32, 2 * c + hh);
     int voff[2][D / 32];
-    {
-        const int g = lane >> 4, vh = g >> 1, dh = g & 1, al = lane & 15;
 #pragma unroll
-        for (int j4 = 0; j4 < 2; ++j4)
+    for (int j4 = 0; j4 < 2; ++j4)
 #pragma unroll
-            for (int dt = 0; dt < D / 32; ++dt) {
-                const int row = 8 * j4 + 4 * vh + (al >> 2);
-                const int col = 32 * dt + 16 * dh + 4 * (al & 3);
-                voff[j4][dt] = TL::off(row, col >> 3) + ((col & 4) << 1);
-            }
-    }
+        for (int dt = 0; dt < D / 32; ++dt) voff[j4][dt] = TL::tr_off(lane, j4, dt);
 
     const int p0 = L.row_ptr[qb];
     const int nblk = L.row_ptr[qb + 1] - p0;

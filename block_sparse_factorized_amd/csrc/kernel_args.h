@@ -46,6 +46,7 @@ struct BwdArgs {
     void* dk;
     void* dv;
     float* delta;  // workspace: D_i = sum_t dO_it * O_it, fp32 [B*H*n]
+    float* nl2;    // workspace: -lse_i * log2(e) (-inf for an empty row), fp32 [B*H*n]
     int64_t n;
     int32_t H;
     int32_t BH;
@@ -58,7 +59,7 @@ struct BwdArgs {
 // Launchers: enqueue one kernel on `stream`, return hipGetLastError().
 hipError_t launch_fwd_bf16_t64(int d, const FwdArgs& a, int n_items, hipStream_t stream);
 hipError_t launch_fwd_f32_t16(int d, const FwdArgs& a, int n_items, hipStream_t stream);
-hipError_t launch_bwd_delta_bf16(int d, const BwdArgs& a, int64_t rows, hipStream_t stream);
+hipError_t launch_bwd_rowterms_bf16(int d, const BwdArgs& a, int64_t rows, hipStream_t stream);
 hipError_t launch_bwd_dkdv_bf16_t64(int d, const BwdArgs& a, int n_items, hipStream_t stream);
 hipError_t launch_bwd_dq_bf16_t64(int d, const BwdArgs& a, int n_items, hipStream_t stream);
 

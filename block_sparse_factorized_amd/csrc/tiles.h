@@ -1,0 +1,98 @@
+// tiles.h -- device helpers shared by the gfx950 kernels of libsa: vector
+// types, bf16 packing, lane-pair exchanges, transposing LDS reads and the
+// swizzled 64-row LDS tile filled by direct global-to-LDS loads.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace sa {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(1))) void glb_void;
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(4))) const uint64_t const_u64;
+typedef __attribute__((address_space(4))) const int32_t const_i32;
+
+__device__ static inline unsigned bf16_pair(float x, float y)
+{
+    return __builtin_bit_cast(unsigned, __builtin_convertvector((f32x2){x, y}, bf16x2));
+}
+
+// Registers first..first+7 of x as eight bf16 (round to nearest even).
+__device__ static inline bf16x8 pack8(const f32x16& x, int first)
+{
+    u32x4 u;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) u[e] = bf16_pair(x[first + 2 * e], x[first + 2 * e + 1]);
+    return __builtin_bit_cast(bf16x8, u);
+}
+
+// Max of x over lanes n and n+32 (lane pairs that hold the same query row).
+__device__ static inline float half_max(float x)
+{
+    auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __builtin_fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
+// The value lane n+32 (or n-32) holds.
+__device__ static inline float swap_halves(float x)
+{
+    auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float((__lane_id() < 32) ? r[1] : r[0]);
+}
+
+__device__ static inline void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }  // vmcnt(0)
+
+// Two transposing 8-byte LDS reads (ds_read_b64_tr_b16) forming one 8 x bf16 operand.
+__device__ static inline bf16x8 lds_read_tr8(const unsigned char* p0, const unsigned char* p1)
+{
+    i16x4 x = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)(lds_void*)p0);
+    i16x4 y = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)(lds_void*)p1);
+    return __builtin_bit_cast(bf16x8, __builtin_shufflevector(x, y, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
+// A 64 x D bf16 tile in LDS: rows unpadded (2*D bytes), each row's 16-byte
+// chunks stored at position chunk ^ swz(row), which spreads the rows that
+// one MFMA operand read touches over all LDS banks.  Filled by direct
+// global-to-LDS loads: load u of wave w writes 1 KB of consecutive slots,
+// lane l the 16 bytes at slot l.
+template <int D>
+struct Tile64 {
+    static constexpr int kRow = 2 * D;
+    static constexpr int kBytes = 64 * kRow;
+    __device__ static inline int swz(int r) { return D == 64 ? ((r >> 1) & 7) : (r & 15); }
+    __device__ static inline int off(int r, int chunk) { return r * kRow + ((chunk ^ swz(r)) << 4); }
+    __device__ static inline int load_dst(int u, int w) { return (2 * u + w) * 1024; }
+    // Byte offset of this lane's half (j4 = 0, 1) of a transposing read that
+    // yields the 32x32x16 A operand [d = 32*dt + lane%32][sequence index
+    // 8*(lane/32) + j] of a 16-row chunk at row 0: lane a of each 16-lane
+    // group addresses row 8*j4 + 4*(group/2) + a/4, columns 32*dt +
+    // 16*(group%2) + 4*(a%4) .. +3, and receives one column of 4 rows.  Add
+    // 16*kRow per further chunk (the swizzle does not depend on it).
+    __device__ static inline int tr_off(int lane, int j4, int dt)
+    {
+        const int g = lane >> 4, al = lane & 15;
+        const int row = 8 * j4 + 4 * (g >> 1) + (al >> 2);
+        const int col = 32 * dt + 16 * (g & 1) + 4 * (al & 3);
+        return off(row, col >> 3) + ((col & 4) << 1);
+    }
+    // Element offset in the global tile of the 16 bytes lane `lane` loads in load u of wave w.
+    __device__ static inline int load_src(int u, int w, int lane)
+    {
+        const int byte = load_dst(u, w) + 16 * lane;
+        const int r = byte / kRow, pos = (byte % kRow) >> 4;
+        return r * D + ((pos ^ swz(r)) << 3);
+    }
+};
+
+
+}  // namespace sa

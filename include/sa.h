@@ -149,7 +149,8 @@ int sa_fwd(const sa_layout_t* const* head_layout, int32_t B, int32_t H, int64_t 
            int dtype, float scale, const void* q, const void* k, const void* v, void* o,
            float* lse, void* stream);
 
-/* Bytes of device workspace sa_bwd needs (the fp32 row terms D_i). */
+/* Bytes of device workspace sa_bwd needs: two fp32 row terms per row, D_i
+ * = sum_t dO_it O_it and -lse_i * log2(e). */
 size_t sa_bwd_workspace_size(int32_t B, int32_t H, int64_t n, int32_t d);
 
 /*
@@ -171,7 +172,8 @@ int sa_bwd(const sa_layout_t* const* head_layout, int32_t B, int32_t H, int64_t 
  * them themselves (for instance dQ and dK/dV on two streams once the row
  * terms are ready).  Arguments mean what they mean for sa_bwd; each call
  * reads and writes only the pointers it takes.
- *   sa_bwd_rowterms  D_i = sum_t dO_it O_it into the workspace
+ *   sa_bwd_rowterms  the row terms D_i = sum_t dO_it O_it and -lse_i log2(e)
+ *                    into the workspace
  *   sa_bwd_dkdv      dK, dV (reads the row terms from the workspace), one
  *                    workgroup per key block walking its query blocks
  *   sa_bwd_dq        dQ (reads the row terms from the workspace), one
@@ -180,15 +182,14 @@ int sa_bwd(const sa_layout_t* const* head_layout, int32_t B, int32_t H, int64_t 
  * device.  Same errors as sa_bwd.
  */
 int sa_bwd_rowterms(const sa_layout_t* const* head_layout, int32_t B, int32_t H, int64_t n, int32_t d,
-                    int dtype, float scale, const void* o, const void* dout, void* workspace,
-                    size_t ws_bytes, void* stream);
+                    int dtype, float scale, const void* o, const float* lse, const void* dout,
+                    void* workspace, size_t ws_bytes, void* stream);
 int sa_bwd_dkdv(const sa_layout_t* const* head_layout, int32_t B, int32_t H, int64_t n, int32_t d,
-                int dtype, float scale, const void* q, const void* k, const void* v, const float* lse,
-                const void* dout, void* dk, void* dv, const void* workspace, size_t ws_bytes,
-                void* stream);
+                int dtype, float scale, const void* q, const void* k, const void* v, const void* dout,
+                void* dk, void* dv, const void* workspace, size_t ws_bytes, void* stream);
 int sa_bwd_dq(const sa_layout_t* const* head_layout, int32_t B, int32_t H, int64_t n, int32_t d,
-              int dtype, float scale, const void* q, const void* k, const void* v, const float* lse,
-              const void* dout, void* dq, const void* workspace, size_t ws_bytes, void* stream);
+              int dtype, float scale, const void* q, const void* k, const void* v, const void* dout,
+              void* dq, const void* workspace, size_t ws_bytes, void* stream);
 
 /* Static text of a status code. */
 const char* sa_status_string(int status);

@@ -252,3 +252,19 @@ def test_img64_dense_comparison_sampled_rows():
         compare_head(x, res, b, h, pats[h], 1.0, False, fp32=False, rows=rows)
 
 
+
+
+def test_backward_stages_match_sa_bwd():
+    """sa_bwd_rowterms + sa_bwd_dkdv + sa_bwd_dq give sa_bwd's results bit for bit."""
+    w = WORKLOADS["text"]
+    x = workloads.make_inputs(w, shape=(1, 2, 1024, 64))
+    pats = w.head_patterns()[:2]
+    lays = layouts_for(pats, 1024, 64)
+    q, k, v, do = (x[t].to(DEV) for t in ("q", "k", "v", "do"))
+    o, lse = sa.sa_fwd(q, k, v, lays, 1.0)
+    dq, dk, dv = sa.sa_bwd(q, k, v, o, lse, do, lays, 1.0)
+    ws = sa.sa_bwd_rowterms(o, lse, do, lays, 1.0)
+    dk2, dv2 = sa.sa_bwd_dkdv(q, k, v, do, lays, 1.0, ws)
+    dq2 = sa.sa_bwd_dq(q, k, v, do, lays, 1.0, ws)
+    torch.cuda.synchronize()
+    assert torch.equal(dq, dq2) and torch.equal(dk, dk2) and torch.equal(dv, dv2)
