@@ -134,6 +134,7 @@ __global__ __launch_bounds__(128) void bwd_dkdv_kernel(const BwdArgs a)
     const int p0 = L.col_ptr[kb];
     const int nblk = L.col_ptr[kb + 1] - p0;
     const float c2 = a.scale_log2;
+    const bf16x8 zero8 = __builtin_bit_cast(bf16x8, (u32x4){0u, 0u, 0u, 0u});
 
     auto issue = [&](int qb, unsigned char* qd, unsigned char* od, float* rd) {
         const unsigned short* Qt = Q + (int64_t)qb * T * D;
@@ -172,43 +173,57 @@ __global__ __launch_bounds__(128) void bwd_dkdv_kernel(const BwdArgs a)
                 dp[qt] = mfma(oa, vop[c], dp[qt]);
             }
         }
-        // P = exp2(c2 s - lse log2 e), dS = P (dP - D).
-#pragma unroll
-        for (int qt = 0; qt < 2; ++qt)
-#pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                const f32x4 nl = *(const f32x4*)&rc[32 * qt + 8 * g + 4 * hh];
-                const f32x4 dd = *(const f32x4*)&rc[T + 32 * qt + 8 * g + 4 * hh];
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int i = 4 * g + e;
-                    const float p = __builtin_amdgcn_exp2f(fmaf(s[qt][i], c2, nl[e]));
-                    s[qt][i] = p;
-                    dp[qt][i] = p * (dp[qt][i] - dd[e]);
-                }
-            }
+        // Masked elements get s = -inf, hence P = exp2(c2 s - lse log2 e) = 0 and
+        // dS = P (dP - D) = 0.  A 32-query half with no allowed element for
+        // this wave's keys has zero P and dS: its elementwise work is skipped,
+        // its products still run.
+        bool live[2] = {true, true};
         if (mid >= 0) {
             const_u64* pl = (const_u64*)(L.planes_t + ((int64_t)mid * 2 + w) * 32);
 #pragma unroll
-            for (int qt = 0; qt < 2; ++qt)
+            for (int qt = 0; qt < 2; ++qt) {
+                uint64_t any = 0;
 #pragma unroll
-                for (int i = 0; i < 16; ++i) {
-                    const bool ok = __builtin_amdgcn_inverse_ballot_w64(pl[16 * qt + i]);
-                    s[qt][i] = ok ? s[qt][i] : 0.f;
-                    dp[qt][i] = ok ? dp[qt][i] : 0.f;
+                for (int i = 0; i < 16; ++i) any |= pl[16 * qt + i];
+                live[qt] = any != 0;
+                if (live[qt]) {
+#pragma unroll
+                    for (int i = 0; i < 16; ++i)
+                        s[qt][i] = __builtin_amdgcn_inverse_ballot_w64(pl[16 * qt + i]) ? s[qt][i] : -INFINITY;
                 }
+            }
         }
 #pragma unroll
-        for (int cc = 0; cc < 4; ++cc) {
-            const bf16x8 pb = pack8(s[cc / 2], 8 * (cc % 2));
-            const bf16x8 db = pack8(dp[cc / 2], 8 * (cc % 2));
+        for (int qt = 0; qt < 2; ++qt) {
+            bf16x8 pb[2] = {zero8, zero8}, db[2] = {zero8, zero8};
+            if (live[qt]) {
 #pragma unroll
-            for (int dt = 0; dt < D / 32; ++dt) {
-                const bf16x8 ot = lds_read_tr8(oc + toff[0][dt] + cc * 16 * TL::kRow, oc + toff[1][dt] + cc * 16 * TL::kRow);
-                const bf16x8 qt8 = lds_read_tr8(qc + toff[0][dt] + cc * 16 * TL::kRow, qc + toff[1][dt] + cc * 16 * TL::kRow);
-                dv[dt] = mfma(ot, pb, dv[dt]);
-                dk[dt] = mfma(qt8, db, dk[dt]);
+                for (int g = 0; g < 4; ++g) {
+                    const f32x4 nl = *(const f32x4*)&rc[32 * qt + 8 * g + 4 * hh];
+                    const f32x4 dd = *(const f32x4*)&rc[T + 32 * qt + 8 * g + 4 * hh];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const int i = 4 * g + e;
+                        const float p = __builtin_amdgcn_exp2f(fmaf(s[qt][i], c2, nl[e]));
+                        s[qt][i] = p;
+                        dp[qt][i] = p * (dp[qt][i] - dd[e]);
+                    }
+                }
+                pb[0] = pack8(s[qt], 0);
+                pb[1] = pack8(s[qt], 8);
+                db[0] = pack8(dp[qt], 0);
+                db[1] = pack8(dp[qt], 8);
             }
+#pragma unroll
+            for (int h = 0; h < 2; ++h)
+#pragma unroll
+                for (int dt = 0; dt < D / 32; ++dt) {
+                    const int cc = 2 * qt + h;
+                    const bf16x8 ot = lds_read_tr8(oc + toff[0][dt] + cc * 16 * TL::kRow, oc + toff[1][dt] + cc * 16 * TL::kRow);
+                    const bf16x8 qt8 = lds_read_tr8(qc + toff[0][dt] + cc * 16 * TL::kRow, qc + toff[1][dt] + cc * 16 * TL::kRow);
+                    dv[dt] = mfma(ot, pb[h], dv[dt]);
+                    dk[dt] = mfma(qt8, db[h], dk[dt]);
+                }
         }
         wait_vmem();
         __syncthreads();
@@ -288,6 +303,7 @@ __global__ __launch_bounds__(128) void bwd_dq_kernel(const BwdArgs a)
     const int p0 = L.row_ptr[qb];
     const int nblk = L.row_ptr[qb + 1] - p0;
     const float c2 = a.scale_log2;
+    const bf16x8 zero8 = __builtin_bit_cast(bf16x8, (u32x4){0u, 0u, 0u, 0u});
 
     auto issue = [&](int kb, unsigned char* kd, unsigned char* vd) {
         const unsigned short* Kt = K + (int64_t)kb * T * D;
@@ -323,30 +339,46 @@ __global__ __launch_bounds__(128) void bwd_dq_kernel(const BwdArgs a)
                 dp[kt] = mfma(va, dop[c], dp[kt]);
             }
         }
-        // Register i of tile kt: key 32*kt + 8*(i/4) + 4*hh + i%4 of query q_local.
-#pragma unroll
-        for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                const float p = __builtin_amdgcn_exp2f(fmaf(s[kt][i], c2, nl2));
-                dp[kt][i] = p * (dp[kt][i] - d_i);
-            }
+        // Register i of tile kt: key 32*kt + 8*(i/4) + 4*hh + i%4 of query
+        // q_local.  Masked elements get s = -inf, so P^T and dS^T = P^T (dP^T -
+        // D) are zero there; a 32-key half with no allowed element for this
+        // wave's queries is skipped.
+        bool live[2] = {true, true};
         if (mid >= 0) {
             const_u64* pl = (const_u64*)(L.planes + ((int64_t)mid * 2 + w) * 32);
 #pragma unroll
-            for (int kt = 0; kt < 2; ++kt)
+            for (int kt = 0; kt < 2; ++kt) {
+                uint64_t any = 0;
 #pragma unroll
-                for (int i = 0; i < 16; ++i)
-                    dp[kt][i] = __builtin_amdgcn_inverse_ballot_w64(pl[16 * kt + i]) ? dp[kt][i] : 0.f;
+                for (int i = 0; i < 16; ++i) any |= pl[16 * kt + i];
+                live[kt] = any != 0;
+                if (live[kt]) {
+#pragma unroll
+                    for (int i = 0; i < 16; ++i)
+                        s[kt][i] = __builtin_amdgcn_inverse_ballot_w64(pl[16 * kt + i]) ? s[kt][i] : -INFINITY;
+                }
+            }
         }
 #pragma unroll
-        for (int cc = 0; cc < 4; ++cc) {
-            const bf16x8 db = pack8(dp[cc / 2], 8 * (cc % 2));
+        for (int kt = 0; kt < 2; ++kt) {
+            bf16x8 db[2] = {zero8, zero8};
+            if (live[kt]) {
 #pragma unroll
-            for (int dt = 0; dt < D / 32; ++dt) {
-                const bf16x8 kt8 = lds_read_tr8(kc + toff[0][dt] + cc * 16 * TL::kRow, kc + toff[1][dt] + cc * 16 * TL::kRow);
-                dq[dt] = mfma(kt8, db, dq[dt]);
+                for (int i = 0; i < 16; ++i) {
+                    const float p = __builtin_amdgcn_exp2f(fmaf(s[kt][i], c2, nl2));
+                    dp[kt][i] = p * (dp[kt][i] - d_i);
+                }
+                db[0] = pack8(dp[kt], 0);
+                db[1] = pack8(dp[kt], 8);
             }
+#pragma unroll
+            for (int h = 0; h < 2; ++h)
+#pragma unroll
+                for (int dt = 0; dt < D / 32; ++dt) {
+                    const int cc = 2 * kt + h;
+                    const bf16x8 kt8 = lds_read_tr8(kc + toff[0][dt] + cc * 16 * TL::kRow, kc + toff[1][dt] + cc * 16 * TL::kRow);
+                    dq[dt] = mfma(kt8, db[h], dq[dt]);
+                }
         }
         wait_vmem();
         __syncthreads();

@@ -14,21 +14,27 @@
 // (batch, head, query block); wave w owns query rows 32w..32w+31.
 //   * The score tile is computed transposed, S^T = K Q^T, with
 //     v_mfma_f32_32x32x16_bf16: lane (hh = lane/32, n = lane%32) then holds
-//     16 keys of query n per 32-key tile, so the row max and row sum are
-//     in-lane reductions plus one exchange with lane n+32.
+//     16 keys of query n per 32-key half, so the row max and row sum are
+//     in-lane reductions plus one exchange with lane n+32 (v_permlane32_swap).
 //   * The output is accumulated transposed too, O^T = V^T P^T, so the
 //     softmax rescale factor of query n is in the lane that owns its output
-//     column.  P^T leaves the score accumulators already in the B-operand
-//     layout, with the keys of each 16-key chunk taken in the order
-//     c*16 + {0-3, 8-11} (lanes 0-31) and {4-7, 12-15} (lanes 32-63); V is
-//     stored transposed in LDS with bits 2 and 3 of the key index swapped so
-//     that each lane reads its 8 keys with one 16-byte LDS load.
-//   * K and V tiles go global -> registers -> LDS with 16-byte loads, double
-//     buffered: the next tile's loads are in flight while the matrix cores
-//     work on the current one, one barrier per tile.
+//     column.  The score accumulators are already the B operand of that
+//     product once each 16-key chunk's keys are taken in the order
+//     {0-3, 8-11} (lanes 0-31) and {4-7, 12-15} (lanes 32-63); the matching
+//     V^T operand comes straight from the row-major V tile through the
+//     transposing LDS read (ds_read_b64_tr_b16).
+//   * K and V tiles go from HBM straight into LDS (global_load_lds_dwordx4)
+//     in a bank-conflict-free swizzled layout.  With d = 64 a single buffer
+//     is used: keeping LDS per workgroup small lets four waves per SIMD
+//     hide the load latency, which measured faster than double buffering.
+//   * Partial blocks are masked with 64-bit lane masks held in SGPRs (one
+//     v_cndmask per element); a 32-key half with no allowed element for the
+//     wave skips its softmax work (its products still run, on zero weights).
+//   * The running max is moved only when a row's max grows by more than
+//     2^8 in the exponent, so the accumulator rescale is rare.
 //
 // f32 kernel (block 16, d 64), one wave per (batch, head, query block), the
-// same structure on v_mfma_f32_16x16x4_f32.
+// same transposed structure on v_mfma_f32_16x16x4_f32.
 #include <hip/hip_runtime.h>
 
 #include "kernel_args.h"
@@ -37,14 +43,15 @@
 namespace sa {
 namespace {
 
-template <int D>
+template <int D, int NBUF>
 __global__ __launch_bounds__(128) void fwd_bf16_t64_kernel(const FwdArgs a)
 {
     constexpr int T = 64;
     typedef Tile64<D> TL;
     constexpr int NI = TL::kBytes / 2048;  // direct-to-LDS loads per wave per tensor
-    __shared__ __attribute__((aligned(1024))) unsigned char kbuf0[TL::kBytes], kbuf1[TL::kBytes];
-    __shared__ __attribute__((aligned(1024))) unsigned char vbuf0[TL::kBytes], vbuf1[TL::kBytes];
+    constexpr int PD = NBUF > 1 ? NBUF - 1 : 0;  // tiles loaded ahead of the one in use
+    __shared__ __attribute__((aligned(1024))) unsigned char kbuf[NBUF][TL::kBytes];
+    __shared__ __attribute__((aligned(1024))) unsigned char vbuf[NBUF][TL::kBytes];
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -88,26 +95,30 @@ __global__ __launch_bounds__(128) void fwd_bf16_t64_kernel(const FwdArgs a)
         for (int i = 0; i < 16; ++i) oacc[dt][i] = 0.f;
     float m_ref = -INFINITY, l_run = 0.f;
     const float c2 = a.scale_log2;
+    const bf16x8 zero8 = __builtin_bit_cast(bf16x8, (u32x4){0u, 0u, 0u, 0u});
 
-    auto issue = [&](int kb, unsigned char* kd, unsigned char* vd) {
+    auto issue = [&](int kb, int buf) {
         const unsigned short* Kt = K + (int64_t)kb * T * D;
         const unsigned short* Vt = V + (int64_t)kb * T * D;
 #pragma unroll
         for (int u = 0; u < NI; ++u) {
-            __builtin_amdgcn_global_load_lds((glb_void*)(Kt + goff[u]), (lds_void*)(kd + TL::load_dst(u, w)), 16, 0, 0);
-            __builtin_amdgcn_global_load_lds((glb_void*)(Vt + goff[u]), (lds_void*)(vd + TL::load_dst(u, w)), 16, 0, 0);
+            __builtin_amdgcn_global_load_lds((glb_void*)(Kt + goff[u]), (lds_void*)(kbuf[buf] + TL::load_dst(u, w)), 16, 0, 0);
+            __builtin_amdgcn_global_load_lds((glb_void*)(Vt + goff[u]), (lds_void*)(vbuf[buf] + TL::load_dst(u, w)), 16, 0, 0);
         }
     };
 
-    if (nblk > 0) issue(L.col_idx[p0], kbuf0, vbuf0);
+    // Prologue: the first PD tiles (one tile when single-buffered).
+#pragma unroll
+    for (int pre = 0; pre < (PD > 0 ? PD : 1); ++pre)
+        if (pre < nblk) issue(L.col_idx[p0 + pre], pre);
     wait_vmem();
     __syncthreads();
 
+    int cur = 0;
     for (int t = 0; t < nblk; ++t) {
-        const bool odd = t & 1;
-        const unsigned char* kc = odd ? kbuf1 : kbuf0;
-        const unsigned char* vc = odd ? vbuf1 : vbuf0;
-        if (t + 1 < nblk) issue(L.col_idx[p0 + t + 1], odd ? kbuf0 : kbuf1, odd ? vbuf0 : vbuf1);
+        const unsigned char* kc = kbuf[cur];
+        const unsigned char* vc = vbuf[cur];
+        if (PD > 0 && t + PD < nblk) issue(L.col_idx[p0 + t + PD], (cur + PD) % NBUF);
         const int mid = L.mask_id[p0 + t];
 
         // S^T = K Q^T: register i of s[kt] holds key 32*kt + 8*(i/4) + 4*hh + i%4 of query n.
@@ -122,22 +133,35 @@ __global__ __launch_bounds__(128) void fwd_bf16_t64_kernel(const FwdArgs a)
                 s[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop, qop[c], s[kt], 0, 0, 0);
             }
         }
-        // Partial block: lane masks of every register, one 64-bit plane each, in SGPRs.
+        // Partial block: lane masks of every register, one 64-bit plane each, in
+        // SGPRs.  A 32-key half with no allowed element in this wave's rows (all
+        // 16 of its planes zero) has only zero weights, so its softmax work is
+        // skipped; its matrix products still run, with zero weights.
+        bool live[2] = {true, true};
         if (mid >= 0) {
             // Read-only for the kernel's lifetime: the constant address space
             // lets these wave-uniform loads go to SGPRs (s_load_dwordx16).
             const_u64* pl = (const_u64*)(L.planes + ((int64_t)mid * 2 + w) * 32);
 #pragma unroll
-            for (int kt = 0; kt < 2; ++kt)
+            for (int kt = 0; kt < 2; ++kt) {
+                uint64_t any = 0;
 #pragma unroll
-                for (int i = 0; i < 16; ++i)
-                    s[kt][i] = __builtin_amdgcn_inverse_ballot_w64(pl[16 * kt + i]) ? s[kt][i] : -INFINITY;
+                for (int i = 0; i < 16; ++i) any |= pl[16 * kt + i];
+                live[kt] = any != 0;
+                if (live[kt]) {
+#pragma unroll
+                    for (int i = 0; i < 16; ++i)
+                        s[kt][i] = __builtin_amdgcn_inverse_ballot_w64(pl[16 * kt + i]) ? s[kt][i] : -INFINITY;
+                }
+            }
         }
-        float mx = s[0][0];
+        float mx = -INFINITY;
 #pragma unroll
-        for (int i = 1; i < 16; ++i) mx = __builtin_fmaxf(mx, s[0][i]);
+        for (int kt = 0; kt < 2; ++kt)
+            if (live[kt]) {
 #pragma unroll
-        for (int i = 0; i < 16; ++i) mx = __builtin_fmaxf(mx, s[1][i]);
+                for (int i = 0; i < 16; ++i) mx = __builtin_fmaxf(mx, s[kt][i]);
+            }
         mx = half_max(mx);
 
         // Lazy rescale: keep the reference max unless some row's max grew by more
@@ -153,31 +177,49 @@ __global__ __launch_bounds__(128) void fwd_bf16_t64_kernel(const FwdArgs a)
             m_ref = m_new;
         }
         const float mc = m_ref == -INFINITY ? 0.f : m_ref * c2;
-        float lsum = 0.f;
-#pragma unroll
-        for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                const float p = __builtin_amdgcn_exp2f(fmaf(s[kt][i], c2, -mc));
-                s[kt][i] = p;
-                lsum += p;
-            }
-        l_run += lsum;
 
-        // O^T += V^T P^T; chunk cc of P^T is registers 8*(cc%2)..+7 of s[cc/2].
+        // P^T (chunk cc of P^T is registers 8*(cc%2)..+7 of s[cc/2]), then
+        // O^T += V^T P^T, one 32-key half at a time.
 #pragma unroll
-        for (int cc = 0; cc < 4; ++cc) {
-            const bf16x8 pb = pack8(s[cc / 2], 8 * (cc % 2));
+        for (int kt = 0; kt < 2; ++kt) {
+            bf16x8 pb[2] = {zero8, zero8};
+            if (live[kt]) {
+                float lsum = 0.f;
 #pragma unroll
-            for (int dt = 0; dt < D / 32; ++dt) {
-                const bf16x8 vop = lds_read_tr8(vc + voff[0][dt] + cc * 16 * TL::kRow,
-                                                vc + voff[1][dt] + cc * 16 * TL::kRow);
-                oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop, pb, oacc[dt], 0, 0, 0);
+                for (int i = 0; i < 16; ++i) {
+                    const float p = __builtin_amdgcn_exp2f(fmaf(s[kt][i], c2, -mc));
+                    s[kt][i] = p;
+                    lsum += p;
+                }
+                l_run += lsum;
+                pb[0] = pack8(s[kt], 0);
+                pb[1] = pack8(s[kt], 8);
             }
+#pragma unroll
+            for (int h = 0; h < 2; ++h)
+#pragma unroll
+                for (int dt = 0; dt < D / 32; ++dt) {
+                    const int cc = 2 * kt + h;
+                    const bf16x8 vop = lds_read_tr8(vc + voff[0][dt] + cc * 16 * TL::kRow,
+                                                    vc + voff[1][dt] + cc * 16 * TL::kRow);
+                    oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop, pb[h], oacc[dt], 0, 0, 0);
+                }
         }
 
-        wait_vmem();
+        if constexpr (PD == 0) {
+            __syncthreads();  // every wave is done with the only buffer
+            if (t + 1 < nblk) issue(L.col_idx[p0 + t + 1], 0);
+            wait_vmem();
+        } else if constexpr (PD >= 2) {
+            if (t + PD < nblk)
+                wait_vmcnt<2 * NI * (PD - 1)>();  // tile t+1 landed; later ones may still fly
+            else
+                wait_vmem();
+        } else {
+            wait_vmem();
+        }
         __syncthreads();
+        cur = (cur + 1 == NBUF) ? 0 : cur + 1;
     }
 
     const float l_tot = l_run + swap_halves(l_run);
@@ -292,9 +334,9 @@ __global__ __launch_bounds__(64) void fwd_f32_t16_d64_kernel(const FwdArgs a)
 hipError_t launch_fwd_bf16_t64(int d, const FwdArgs& a, int n_items, hipStream_t stream)
 {
     if (d == 64)
-        hipLaunchKernelGGL(fwd_bf16_t64_kernel<64>, dim3(n_items), dim3(128), 0, stream, a);
+        hipLaunchKernelGGL((fwd_bf16_t64_kernel<64, 1>), dim3(n_items), dim3(128), 0, stream, a);
     else
-        hipLaunchKernelGGL(fwd_bf16_t64_kernel<128>, dim3(n_items), dim3(128), 0, stream, a);
+        hipLaunchKernelGGL((fwd_bf16_t64_kernel<128, 2>), dim3(n_items), dim3(128), 0, stream, a);
     return hipGetLastError();
 }
 

@@ -6,6 +6,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+
 namespace sa {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
@@ -52,6 +53,14 @@ __device__ static inline float swap_halves(float x)
 
 __device__ static inline void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }  // vmcnt(0)
 
+// s_waitcnt vmcnt(N), other counters not waited on (gfx9 encoding).
+template <int N>
+__device__ static inline void wait_vmcnt()
+{
+    static_assert(N >= 0 && N < 64, "vmcnt is 6 bits");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
 // Two transposing 8-byte LDS reads (ds_read_b64_tr_b16) forming one 8 x bf16 operand.
 __device__ static inline bf16x8 lds_read_tr8(const unsigned char* p0, const unsigned char* p1)
 {
@@ -69,7 +78,20 @@ template <int D>
 struct Tile64 {
     static constexpr int kRow = 2 * D;
     static constexpr int kBytes = 64 * kRow;
-    __device__ static inline int swz(int r) { return D == 64 ? ((r >> 1) & 7) : (r & 15); }
+    // Row swizzle, for the 64-bank LDS (256 bytes per bank cycle): with d = 64
+    // a row is half a bank cycle, so 16 rows of one chunk (a 16-byte MFMA
+    // operand read, 16 lanes per cycle) need distinct positions within each
+    // row parity, and the 4-row x 32-byte footprints of a transposing read
+    // (32 lanes per cycle) need rows r and r+2 in different aligned 4-chunk
+    // groups: the bit-reversed (r/2) mod 8 gives both.  With d = 128 a row is
+    // a full bank cycle: 16 consecutive rows need distinct positions and any
+    // 4 consecutive rows distinct aligned 4-chunk groups.  Both depend only on
+    // r mod 16, so tile rows 16 apart share offsets.
+    __device__ static inline int swz(int r)
+    {
+        if (D == 64) return ((r >> 1) & 1) << 2 | ((r >> 2) & 1) << 1 | ((r >> 3) & 1);
+        return ((r & 3) << 2) | ((r >> 2) & 3);
+    }
     __device__ static inline int off(int r, int chunk) { return r * kRow + ((chunk ^ swz(r)) << 4); }
     __device__ static inline int load_dst(int u, int w) { return (2 * u + w) * 1024; }
     // Byte offset of this lane's half (j4 = 0, 1) of a transposing read that
