@@ -53,7 +53,8 @@ int device_layout(sa_layout* L, int dev, DevLayout* out)
     auto al = [](size_t x) { return (x + 255) & ~(size_t)255; };
     size_t off_masks = 0;
     size_t off_masks_t = al(off_masks + nwords * 8);
-    const size_t nplanes = L->T == 64 ? (size_t)L->n_masks * 64 : 0;
+    // At least one plane set, so kernels may always load set 0.
+    const size_t nplanes = L->T == 64 ? (size_t)std::max<int64_t>(L->n_masks, 1) * 64 : 0;
     size_t off_planes = al(off_masks_t + nwords * 8);
     size_t off_planes_t = al(off_planes + nplanes * 8);
     size_t off_row_ptr = al(off_planes_t + nplanes * 8);
@@ -62,7 +63,16 @@ int device_layout(sa_layout* L, int dev, DevLayout* out)
     size_t off_col_ptr = al(off_mask_id + nnz * 4);
     size_t off_row_idx = al(off_col_ptr + nqb1 * 4);
     size_t off_col_mask = al(off_row_idx + nnz * 4);
-    size_t total = al(off_col_mask + nnz * 4);
+    const Groups* gs[2] = {&L->qgroups, &L->kgroups};
+    size_t off_gptr[2], off_gblk[2], off_gstep[2];
+    size_t cur = al(off_col_mask + nnz * 4);
+    for (int k = 0; k < 2; ++k) {
+        off_gptr[k] = cur;
+        off_gblk[k] = al(off_gptr[k] + gs[k]->ptr.size() * 4);
+        off_gstep[k] = al(off_gblk[k] + gs[k]->blk.size() * 4);
+        cur = al(off_gstep[k] + gs[k]->step.size() * 4);
+    }
+    size_t total = cur;
     std::vector<unsigned char> host(total, 0);
     if (nwords) {
         memcpy(&host[off_masks], L->masks.data(), nwords * 8);
@@ -82,6 +92,8 @@ int device_layout(sa_layout* L, int dev, DevLayout* out)
     if (nplanes) {
         uint64_t* pl = (uint64_t*)&host[off_planes];
         uint64_t* pt = (uint64_t*)&host[off_planes_t];
+        std::fill(pl, pl + nplanes, ~0ull);
+        std::fill(pt, pt + nplanes, ~0ull);
         auto bit = [&](int64_t m, int r, int s2) {
             int64_t e = (int64_t)r * 64 + s2;
             return (L->masks[m * 64 + (e >> 6)] >> (e & 63)) & 1ull;
@@ -111,6 +123,11 @@ int device_layout(sa_layout* L, int dev, DevLayout* out)
         memcpy(&host[off_col_mask], col_mask.data(), nnz * 4);
     }
     memcpy(&host[off_col_ptr], L->col_ptr.data(), nqb1 * 4);
+    for (int k = 0; k < 2; ++k) {
+        memcpy(&host[off_gptr[k]], gs[k]->ptr.data(), gs[k]->ptr.size() * 4);
+        if (!gs[k]->blk.empty()) memcpy(&host[off_gblk[k]], gs[k]->blk.data(), gs[k]->blk.size() * 4);
+        if (!gs[k]->step.empty()) memcpy(&host[off_gstep[k]], gs[k]->step.data(), gs[k]->step.size() * 4);
+    }
     void* mem = nullptr;
     hipError_t e = hipMalloc(&mem, total);
     if (e != hipSuccess) return fail(SA_ERR_ALLOC, "layout upload: hipMalloc(%zu): %s", total, hipGetErrorString(e));
@@ -131,6 +148,12 @@ int device_layout(sa_layout* L, int dev, DevLayout* out)
     v.col_ptr = (const int32_t*)(b + off_col_ptr);
     v.row_idx = (const int32_t*)(b + off_row_idx);
     v.col_mask = (const int32_t*)(b + off_col_mask);
+    v.qgrp_ptr = (const int32_t*)(b + off_gptr[0]);
+    v.qgrp_blk = (const int2*)(b + off_gblk[0]);
+    v.qgrp_step = (const int4*)(b + off_gstep[0]);
+    v.kgrp_ptr = (const int32_t*)(b + off_gptr[1]);
+    v.kgrp_blk = (const int2*)(b + off_gblk[1]);
+    v.kgrp_step = (const int4*)(b + off_gstep[1]);
     L->dev_mem[dev] = mem;
     L->dev[dev] = v;
     *out = v;
@@ -141,7 +164,7 @@ int device_layout(sa_layout* L, int dev, DevLayout* out)
 // Work lists.  One item per (batch*head, block); ordered longest first so the
 // heaviest blocks start early and the tail is made of short ones.  Cached per
 // (kind, device, B, H, layouts).
-enum ListKind { kByQuery = 0, kByKey = 1 };
+enum ListKind { kByQuery = 0, kByKey = 1, kByQueryPair = 2 };
 
 struct Plan {
     Item* items;
@@ -162,15 +185,17 @@ int get_plan(ListKind kind, int dev, int32_t B, int32_t H, sa_layout* const* hl,
         *out = it->second;
         return SA_OK;
     }
-    const int64_t nqb = hl[0]->nqb;
-    const int64_t count = (int64_t)B * H * nqb;
+    auto listing = [&](const sa_layout* L) -> const std::vector<int32_t>& {
+        return kind == kByQuery ? L->row_ptr : kind == kByKey ? L->col_ptr : L->qgroups.ptr;
+    };
+    int64_t count = 0;
+    for (int32_t bh = 0; bh < B * H; ++bh) count += (int64_t)listing(hl[bh % H]).size() - 1;
     std::vector<Item> items((size_t)count);
     std::vector<int32_t> cost((size_t)count);
     size_t x = 0;
     for (int32_t bh = 0; bh < B * H; ++bh) {
-        const sa_layout* L = hl[bh % H];
-        const std::vector<int32_t>& ptr = kind == kByQuery ? L->row_ptr : L->col_ptr;
-        for (int64_t blk = 0; blk < nqb; ++blk, ++x) {
+        const std::vector<int32_t>& ptr = listing(hl[bh % H]);
+        for (int64_t blk = 0; blk + 1 < (int64_t)ptr.size(); ++blk, ++x) {
             items[x] = Item{bh, (int32_t)blk};
             cost[x] = ptr[blk + 1] - ptr[blk];
         }
@@ -331,7 +356,7 @@ int sa_fwd(const sa_layout_t* const* head_layout, int32_t B, int32_t H, int64_t 
     st = prepare_device(distinct, nl, &ht, &dev);
     if (st != SA_OK) return st;
     Plan plan;
-    st = get_plan(kByQuery, dev, B, H, hl.data(), &plan);
+    st = get_plan(dtype == SA_BF16 ? kByQueryPair : kByQuery, dev, B, H, hl.data(), &plan);
     if (st != SA_OK) return st;
     FwdArgs a;
     a.q = q;

@@ -44,27 +44,33 @@ namespace sa {
 namespace {
 
 template <int D, int NBUF>
-__global__ __launch_bounds__(128) void fwd_bf16_t64_kernel(const FwdArgs a)
+__global__ __launch_bounds__(256) void fwd_bf16_t64_kernel(const FwdArgs a)
 {
     constexpr int T = 64;
-    typedef Tile64<D> TL;
-    constexpr int NI = TL::kBytes / 2048;  // direct-to-LDS loads per wave per tensor
+    typedef Tile64<D, 4> TL;
+    constexpr int NI = TL::kLoads;  // direct-to-LDS loads per wave per tensor
     constexpr int PD = NBUF > 1 ? NBUF - 1 : 0;  // tiles loaded ahead of the one in use
     __shared__ __attribute__((aligned(1024))) unsigned char kbuf[NBUF][TL::kBytes];
     __shared__ __attribute__((aligned(1024))) unsigned char vbuf[NBUF][TL::kBytes];
 
+    // Work item: a pair of query blocks of one (batch, head) with nearly the
+    // same key list; waves 0-1 own the rows of the first block, waves 2-3 the
+    // rows of the second.  The K/V tiles of the merged list are shared.
     const int tid = threadIdx.x, lane = tid & 63;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int member = w >> 1, wr = w & 1;
     const int n32 = lane & 31, hh = lane >> 5;
     const Item item = a.items[blockIdx.x];
-    const int bh = item.bh, qb = item.blk;
+    const int bh = item.bh, grp = item.blk;
     const DevLayout L = a.heads.lay[a.heads.head_lay[bh % a.H]];
+    const int2 pair = L.qgrp_blk[grp];
+    const int qb = member ? pair.y : pair.x;  // -1: this wave has no rows
     const int64_t head = (int64_t)bh * a.n * D;
     const unsigned short* Q = (const unsigned short*)a.q + head;
     const unsigned short* K = (const unsigned short*)a.k + head;
     const unsigned short* V = (const unsigned short*)a.v + head;
-    const int q_local = 32 * w + n32;
-    const int64_t q_row = (int64_t)qb * T + q_local;
+    const int q_local = 32 * wr + n32;
+    const int64_t q_row = (int64_t)(qb < 0 ? 0 : qb) * T + q_local;
 
     // Q^T as the B operand of S^T = K Q^T: lane (hh, n) holds d = 16c + 8hh .. +7 of query n.
     bf16x8 qop[D / 16];
@@ -85,8 +91,8 @@ __global__ __launch_bounds__(128) void fwd_bf16_t64_kernel(const FwdArgs a)
 #pragma unroll
         for (int dt = 0; dt < D / 32; ++dt) voff[j4][dt] = TL::tr_off(lane, j4, dt);
 
-    const int p0 = L.row_ptr[qb];
-    const int nblk = L.row_ptr[qb + 1] - p0;
+    const int p0 = L.qgrp_ptr[grp];
+    const int nblk = L.qgrp_ptr[grp + 1] - p0;
 
     f32x16 oacc[D / 32];
 #pragma unroll
@@ -110,7 +116,7 @@ __global__ __launch_bounds__(128) void fwd_bf16_t64_kernel(const FwdArgs a)
     // Prologue: the first PD tiles (one tile when single-buffered).
 #pragma unroll
     for (int pre = 0; pre < (PD > 0 ? PD : 1); ++pre)
-        if (pre < nblk) issue(L.col_idx[p0 + pre], pre);
+        if (pre < nblk) issue(L.qgrp_step[p0 + pre].x, pre);
     wait_vmem();
     __syncthreads();
 
@@ -118,42 +124,59 @@ __global__ __launch_bounds__(128) void fwd_bf16_t64_kernel(const FwdArgs a)
     for (int t = 0; t < nblk; ++t) {
         const unsigned char* kc = kbuf[cur];
         const unsigned char* vc = vbuf[cur];
-        if (PD > 0 && t + PD < nblk) issue(L.col_idx[p0 + t + PD], (cur + PD) % NBUF);
-        const int mid = L.mask_id[p0 + t];
+        if (PD > 0 && t + PD < nblk) issue(L.qgrp_step[p0 + t + PD].x, (cur + PD) % NBUF);
+        const int4 step = L.qgrp_step[p0 + t];
+        const int mid = member ? step.z : step.y;  // -2: not in this block's list
+        if (qb >= 0 && mid != -2) {
+
+        // Lane masks of every score register, one 64-bit plane each, loaded
+        // into SGPRs before the products so the loads overlap them (a full
+        // block reads plane set 0, unused).  The constant address space lets
+        // these wave-uniform loads be scalar loads.
+        const_u64* pl = (const_u64*)(L.planes + ((int64_t)(mid >= 0 ? mid : 0) * 2 + wr) * 32);
+        uint64_t pln[32];
+#pragma unroll
+        for (int r = 0; r < 32; ++r) pln[r] = pl[r];
+        // A 32-key half with no allowed element in this wave's rows (all 16 of
+        // its planes zero) has only zero weights, so its softmax work is
+        // skipped; its matrix products still run, with zero weights.
+        bool live[2];
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt) {
+            uint64_t any = 0;
+#pragma unroll
+            for (int i = 0; i < 16; ++i) any |= pln[16 * kt + i];
+            live[kt] = mid < 0 || any != 0;
+        }
 
         // S^T = K Q^T: register i of s[kt] holds key 32*kt + 8*(i/4) + 4*hh + i%4 of query n.
+        // All operand reads first, then the products.
         f32x16 s[2];
+        bf16x8 kop[2][D / 16];
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+            for (int c = 0; c < D / 16; ++c) kop[kt][c] = *(const bf16x8*)(kc + koff[c] + kt * 32 * TL::kRow);
 #pragma unroll
         for (int kt = 0; kt < 2; ++kt) {
 #pragma unroll
             for (int i = 0; i < 16; ++i) s[kt][i] = 0.f;
 #pragma unroll
-            for (int c = 0; c < D / 16; ++c) {
-                const bf16x8 kop = *(const bf16x8*)(kc + koff[c] + kt * 32 * TL::kRow);
-                s[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop, qop[c], s[kt], 0, 0, 0);
-            }
+            for (int c = 0; c < D / 16; ++c)
+                s[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop[kt][c], qop[c], s[kt], 0, 0, 0);
         }
-        // Partial block: lane masks of every register, one 64-bit plane each, in
-        // SGPRs.  A 32-key half with no allowed element in this wave's rows (all
-        // 16 of its planes zero) has only zero weights, so its softmax work is
-        // skipped; its matrix products still run, with zero weights.
-        bool live[2] = {true, true};
+        __builtin_amdgcn_sched_group_barrier(0x100, D / 8, 0);  // LDS reads
+        __builtin_amdgcn_sched_group_barrier(0x008, D / 8, 0);  // MFMA
+
+        // Partial block: disallowed elements to -inf.
         if (mid >= 0) {
-            // Read-only for the kernel's lifetime: the constant address space
-            // lets these wave-uniform loads go to SGPRs (s_load_dwordx16).
-            const_u64* pl = (const_u64*)(L.planes + ((int64_t)mid * 2 + w) * 32);
 #pragma unroll
-            for (int kt = 0; kt < 2; ++kt) {
-                uint64_t any = 0;
-#pragma unroll
-                for (int i = 0; i < 16; ++i) any |= pl[16 * kt + i];
-                live[kt] = any != 0;
+            for (int kt = 0; kt < 2; ++kt)
                 if (live[kt]) {
 #pragma unroll
                     for (int i = 0; i < 16; ++i)
-                        s[kt][i] = __builtin_amdgcn_inverse_ballot_w64(pl[16 * kt + i]) ? s[kt][i] : -INFINITY;
+                        s[kt][i] = __builtin_amdgcn_inverse_ballot_w64(pln[16 * kt + i]) ? s[kt][i] : -INFINITY;
                 }
-            }
         }
         float mx = -INFINITY;
 #pragma unroll
@@ -179,9 +202,19 @@ __global__ __launch_bounds__(128) void fwd_bf16_t64_kernel(const FwdArgs a)
         const float mc = m_ref == -INFINITY ? 0.f : m_ref * c2;
 
         // P^T (chunk cc of P^T is registers 8*(cc%2)..+7 of s[cc/2]), then
-        // O^T += V^T P^T, one 32-key half at a time.
+        // O^T += V^T P^T, one 32-key half at a time; the half's V^T operands
+        // are read before its exponentials so the LDS latency overlaps them.
 #pragma unroll
         for (int kt = 0; kt < 2; ++kt) {
+            bf16x8 vop[2][D / 32];
+#pragma unroll
+            for (int h = 0; h < 2; ++h)
+#pragma unroll
+                for (int dt = 0; dt < D / 32; ++dt) {
+                    const int cc = 2 * kt + h;
+                    vop[h][dt] = lds_read_tr8(vc + voff[0][dt] + cc * 16 * TL::kRow,
+                                              vc + voff[1][dt] + cc * 16 * TL::kRow);
+                }
             bf16x8 pb[2] = {zero8, zero8};
             if (live[kt]) {
                 float lsum = 0.f;
@@ -198,17 +231,15 @@ __global__ __launch_bounds__(128) void fwd_bf16_t64_kernel(const FwdArgs a)
 #pragma unroll
             for (int h = 0; h < 2; ++h)
 #pragma unroll
-                for (int dt = 0; dt < D / 32; ++dt) {
-                    const int cc = 2 * kt + h;
-                    const bf16x8 vop = lds_read_tr8(vc + voff[0][dt] + cc * 16 * TL::kRow,
-                                                    vc + voff[1][dt] + cc * 16 * TL::kRow);
-                    oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop, pb[h], oacc[dt], 0, 0, 0);
-                }
+                for (int dt = 0; dt < D / 32; ++dt)
+                    oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop[h][dt], pb[h], oacc[dt], 0, 0, 0);
         }
+
+        }  // this wave's block lists the key block
 
         if constexpr (PD == 0) {
             __syncthreads();  // every wave is done with the only buffer
-            if (t + 1 < nblk) issue(L.col_idx[p0 + t + 1], 0);
+            if (t + 1 < nblk) issue(L.qgrp_step[p0 + t + 1].x, 0);
             wait_vmem();
         } else if constexpr (PD >= 2) {
             if (t + PD < nblk)
@@ -222,6 +253,7 @@ __global__ __launch_bounds__(128) void fwd_bf16_t64_kernel(const FwdArgs a)
         cur = (cur + 1 == NBUF) ? 0 : cur + 1;
     }
 
+    if (qb < 0) return;
     const float l_tot = l_run + swap_halves(l_run);
     const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
     unsigned short* O = (unsigned short*)a.o + head + q_row * D;
@@ -333,10 +365,13 @@ __global__ __launch_bounds__(64) void fwd_f32_t16_d64_kernel(const FwdArgs a)
 
 hipError_t launch_fwd_bf16_t64(int d, const FwdArgs& a, int n_items, hipStream_t stream)
 {
+#ifndef SA_FWD_NBUF
+#define SA_FWD_NBUF 2
+#endif
     if (d == 64)
-        hipLaunchKernelGGL((fwd_bf16_t64_kernel<64, 1>), dim3(n_items), dim3(128), 0, stream, a);
+        hipLaunchKernelGGL((fwd_bf16_t64_kernel<64, SA_FWD_NBUF>), dim3(n_items), dim3(256), 0, stream, a);
     else
-        hipLaunchKernelGGL((fwd_bf16_t64_kernel<128, 2>), dim3(n_items), dim3(128), 0, stream, a);
+        hipLaunchKernelGGL((fwd_bf16_t64_kernel<128, 2>), dim3(n_items), dim3(256), 0, stream, a);
     return hipGetLastError();
 }
 

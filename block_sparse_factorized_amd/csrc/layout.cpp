@@ -122,6 +122,58 @@ uint64_t next_serial()
 
 }  // namespace
 
+// Greedy pairing: each block, in ascending order, takes the unpaired block
+// among the next four whose list has the largest Jaccard similarity with its
+// own, if that is at least 1/2 (two empty lists count as similar).  Strided
+// B with l = 2T pairs qb with qb+2, dense and fixed patterns pair neighbours.
+Groups pair_blocks(const std::vector<int32_t>& ptr, const std::vector<int32_t>& idx,
+                   const std::vector<int32_t>& mask)
+{
+    const int64_t nb = (int64_t)ptr.size() - 1;
+    auto jac = [&](int64_t x, int64_t y) {
+        int32_t i = ptr[x], j = ptr[y], ie = ptr[x + 1], je = ptr[y + 1];
+        if (ie == i && je == j) return 1.0;
+        int64_t inter = 0, uni = 0;
+        while (i < ie || j < je) {
+            if (j >= je || (i < ie && idx[i] < idx[j])) ++i;
+            else if (i >= ie || idx[j] < idx[i]) ++j;
+            else { ++i; ++j; ++inter; }
+            ++uni;
+        }
+        return (double)inter / (double)uni;
+    };
+    Groups g;
+    std::vector<char> used(nb, 0);
+    g.ptr.push_back(0);
+    for (int64_t x = 0; x < nb; ++x) {
+        if (used[x]) continue;
+        int64_t best = -1;
+        double bj = 0.5;
+        for (int64_t y = x + 1; y < std::min<int64_t>(nb, x + 5); ++y) {
+            if (used[y]) continue;
+            double jv = jac(x, y);
+            if (jv >= bj) {
+                if (best < 0 || jv > bj) { best = y; bj = jv; }
+            }
+        }
+        used[x] = 1;
+        if (best >= 0) used[best] = 1;
+        g.blk.push_back((int32_t)x);
+        g.blk.push_back((int32_t)best);
+        int32_t i = ptr[x], ie = ptr[x + 1];
+        int32_t j = best >= 0 ? ptr[best] : 0, je = best >= 0 ? ptr[best + 1] : 0;
+        while (i < ie || j < je) {
+            int32_t o, ma = -2, mb = -2;
+            if (j >= je || (i < ie && idx[i] < idx[j])) { o = idx[i]; ma = mask[i]; ++i; }
+            else if (i >= ie || idx[j] < idx[i]) { o = idx[j]; mb = mask[j]; ++j; }
+            else { o = idx[i]; ma = mask[i]; mb = mask[j]; ++i; ++j; }
+            g.step.insert(g.step.end(), {o, ma, mb, 0});
+        }
+        g.ptr.push_back((int32_t)(g.step.size() / 4));
+    }
+    return g;
+}
+
 int build_layout(int pattern, int64_t n, int64_t l, int64_t c, int32_t block, sa_layout** out)
 {
     if (!out) return fail(SA_ERR_INVALID_ARG, "sa_layout_build: out is NULL");
@@ -205,6 +257,10 @@ int build_layout(int pattern, int64_t n, int64_t l, int64_t c, int32_t block, sa
                 L->row_idx[slot] = (int32_t)qb;
                 L->csr_pos[slot] = a;
             }
+        L->qgroups = pair_blocks(L->row_ptr, L->col_idx, L->mask_id);
+        std::vector<int32_t> col_mask(L->nnz);
+        for (int64_t a = 0; a < L->nnz; ++a) col_mask[a] = L->mask_id[L->csr_pos[a]];
+        L->kgroups = pair_blocks(L->col_ptr, L->row_idx, col_mask);
     } catch (const std::bad_alloc&) {
         delete L;
         return fail(SA_ERR_ALLOC, "sa_layout_build: out of host memory");

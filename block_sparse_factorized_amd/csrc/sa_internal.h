@@ -1,6 +1,7 @@
 // sa_internal.h -- shared host/device declarations of libsa (not installed).
 #pragma once
 
+#include <hip/hip_runtime.h>
 #include <stdint.h>
 
 #include <map>
@@ -34,7 +35,28 @@ struct DevLayout {
     const int32_t* col_ptr;   // [nqb+1]   listing by key block
     const int32_t* row_idx;   // [nnz]     query blocks, ascending per key block
     const int32_t* col_mask;  // [nnz]     mask id of each transposed entry
+    // Pairs of blocks with nearly the same list, walked together by one
+    // workgroup (qgrp: query blocks over their key lists; kgrp: key blocks
+    // over their query lists).  Group g has members grp_blk[g] = {a, b}
+    // (b = -1 for a single block) and steps grp_ptr[g] .. grp_ptr[g+1]-1;
+    // step = {other block, mask of a, mask of b, 0}, mask -1 = full block,
+    // -2 = that member does not list this block.
+    const int32_t* qgrp_ptr;
+    const int2* qgrp_blk;
+    const int4* qgrp_step;
+    const int32_t* kgrp_ptr;
+    const int2* kgrp_blk;
+    const int4* kgrp_step;
 };
+
+// Host-side pairing of one listing (see DevLayout).
+struct Groups {
+    std::vector<int32_t> ptr;
+    std::vector<int32_t> blk;   // 2 per group
+    std::vector<int32_t> step;  // 4 per step
+};
+Groups pair_blocks(const std::vector<int32_t>& ptr, const std::vector<int32_t>& idx,
+                   const std::vector<int32_t>& mask);
 
 }  // namespace sa
 
@@ -47,6 +69,7 @@ struct sa_layout {
     std::vector<int32_t> row_ptr, col_idx, mask_id;
     std::vector<uint64_t> masks;
     std::vector<int32_t> col_ptr, row_idx, csr_pos;
+    sa::Groups qgroups, kgroups;  // pairs by query block / by key block
 
     std::mutex mu;                       // guards dev
     std::map<int, void*> dev_mem;        // device id -> allocation

@@ -72,12 +72,13 @@ __device__ static inline bf16x8 lds_read_tr8(const unsigned char* p0, const unsi
 // A 64 x D bf16 tile in LDS: rows unpadded (2*D bytes), each row's 16-byte
 // chunks stored at position chunk ^ swz(row), which spreads the rows that
 // one MFMA operand read touches over all LDS banks.  Filled by direct
-// global-to-LDS loads: load u of wave w writes 1 KB of consecutive slots,
-// lane l the 16 bytes at slot l.
-template <int D>
+// global-to-LDS loads shared by the NW waves of a workgroup: load u of wave w
+// writes 1 KB of consecutive slots, lane l the 16 bytes at slot l.
+template <int D, int NW = 2>
 struct Tile64 {
     static constexpr int kRow = 2 * D;
     static constexpr int kBytes = 64 * kRow;
+    static constexpr int kLoads = kBytes / (1024 * NW);  // direct-to-LDS loads per wave
     // Row swizzle, for the 64-bank LDS (256 bytes per bank cycle): with d = 64
     // a row is half a bank cycle, so 16 rows of one chunk (a 16-byte MFMA
     // operand read, 16 lanes per cycle) need distinct positions within each
@@ -93,7 +94,14 @@ struct Tile64 {
         return ((r & 3) << 2) | ((r >> 2) & 3);
     }
     __device__ static inline int off(int r, int chunk) { return r * kRow + ((chunk ^ swz(r)) << 4); }
-    __device__ static inline int load_dst(int u, int w) { return (2 * u + w) * 1024; }
+    __device__ static inline int load_dst(int u, int w) { return (NW * u + w) * 1024; }
+    // Element offset in the global tile of the 16 bytes lane `lane` loads in load u of wave w.
+    __device__ static inline int load_src(int u, int w, int lane)
+    {
+        const int byte = load_dst(u, w) + 16 * lane;
+        const int r = byte / kRow, pos = (byte % kRow) >> 4;
+        return r * D + ((pos ^ swz(r)) << 3);
+    }
     // Byte offset of this lane's half (j4 = 0, 1) of a transposing read that
     // yields the 32x32x16 A operand [d = 32*dt + lane%32][sequence index
     // 8*(lane/32) + j] of a 16-row chunk at row 0: lane a of each 16-lane
@@ -106,13 +114,6 @@ struct Tile64 {
         const int row = 8 * j4 + 4 * (g >> 1) + (al >> 2);
         const int col = 32 * dt + 16 * (g & 1) + 4 * (al & 3);
         return off(row, col >> 3) + ((col & 4) << 1);
-    }
-    // Element offset in the global tile of the 16 bytes lane `lane` loads in load u of wave w.
-    __device__ static inline int load_src(int u, int w, int lane)
-    {
-        const int byte = load_dst(u, w) + 16 * lane;
-        const int r = byte / kRow, pos = (byte % kRow) >> 4;
-        return r * D + ((pos ^ swz(r)) << 3);
     }
 };
 
