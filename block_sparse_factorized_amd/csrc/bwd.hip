@@ -8,9 +8,11 @@
 //     D_i   = sum_t dO_it O_it           (row-term kernel)
 //     dP_ij = dO_i . v_j,   dS_ij = P_ij (dP_ij - D_i)
 //     dV_j  = sum_i P_ij dO_i,  dK_j = c sum_i dS_ij q_i   (dK/dV kernel,
-//             one workgroup per key block, walking its query blocks)
+//             one workgroup per pair of key blocks, walking their merged
+//             query-block lists)
 //     dQ_i  = c sum_j dS_ij k_j                             (dQ kernel, one
-//             workgroup per query block, walking its key blocks)
+//             workgroup per pair of query blocks, walking their merged
+//             key-block lists)
 // Both kernels write their outputs once, with no atomics, so results are
 // deterministic.
 //
@@ -72,36 +74,41 @@ __global__ __launch_bounds__(256) void bwd_rowterms_kernel(const BwdArgs a, int6
 }
 
 // ---------------------------------------------------------------------------
-// dK, dV: workgroup = key block (bh, kb), wave w owns keys 32w..32w+31 and
-// walks the query blocks that list kb.  Lane (hh, n) holds key 32w + n.
+// dK, dV: workgroup = a pair of key blocks of one (batch, head) with nearly
+// the same query list (waves 0-1: keys of the first, waves 2-3: keys of the
+// second), walking the merged query list with shared, double-buffered Q/dO
+// tiles and row terms.  Lane (hh, n) of wave w holds key 32*(w%2) + n.
 //   S    = Q K^T     C[q][key]  A = Q rows (LDS)          B = K^T (registers)
 //   dP   = dO V^T    C[q][key]  A = dO rows (LDS)         B = V^T (registers)
 //   dV^T += dO^T P   C[d][key]  A = dO^T (transposing LDS read)  B = P
 //   dK^T += Q^T dS   C[d][key]  A = Q^T (transposing LDS read)   B = dS
 // Register i of an S or dP tile qt holds query 32*qt + 8*(i/4) + 4*hh + i%4.
 template <int D>
-__global__ __launch_bounds__(128) void bwd_dkdv_kernel(const BwdArgs a)
+__global__ __launch_bounds__(256) void bwd_dkdv_kernel(const BwdArgs a)
 {
     constexpr int T = 64;
-    typedef Tile64<D> TL;
-    constexpr int NI = TL::kBytes / 2048;
-    __shared__ __attribute__((aligned(1024))) unsigned char qbuf0[TL::kBytes], qbuf1[TL::kBytes];
-    __shared__ __attribute__((aligned(1024))) unsigned char obuf0[TL::kBytes], obuf1[TL::kBytes];
-    __shared__ __attribute__((aligned(16))) float rbuf0[2 * T], rbuf1[2 * T];  // nl2[64], then D[64]
+    typedef Tile64<D, 4> TL;
+    constexpr int NI = TL::kLoads;
+    __shared__ __attribute__((aligned(1024))) unsigned char qbuf[2][TL::kBytes];
+    __shared__ __attribute__((aligned(1024))) unsigned char obuf[2][TL::kBytes];
+    __shared__ __attribute__((aligned(16))) float rbuf[2][2 * T];  // nl2[64], then D[64]
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int member = w >> 1, wr = w & 1;
     const int n32 = lane & 31, hh = lane >> 5;
     const Item item = a.items[blockIdx.x];
-    const int bh = item.bh, kb = item.blk;
+    const int bh = item.bh, grp = item.blk;
     const DevLayout L = a.heads.lay[a.heads.head_lay[bh % a.H]];
+    const int2 pair = L.kgrp_blk[grp];
+    const int kb = member ? pair.y : pair.x;  // -1: this wave has no keys
     const int64_t head = (int64_t)bh * a.n * D;
     const unsigned short* Q = (const unsigned short*)a.q + head;
     const unsigned short* dO = (const unsigned short*)a.dout + head;
     const float* nl2g = a.nl2 + (int64_t)bh * a.n;
     const float* dlg = a.delta + (int64_t)bh * a.n;
-    const int k_local = 32 * w + n32;
-    const int64_t k_row = (int64_t)kb * T + k_local;
+    const int k_local = 32 * wr + n32;
+    const int64_t k_row = (int64_t)(kb < 0 ? 0 : kb) * T + k_local;
 
     bf16x8 kop[D / 16], vop[D / 16];
     {
@@ -131,104 +138,135 @@ __global__ __launch_bounds__(128) void bwd_dkdv_kernel(const BwdArgs a)
         zero(dk[dt]);
         zero(dv[dt]);
     }
-    const int p0 = L.col_ptr[kb];
-    const int nblk = L.col_ptr[kb + 1] - p0;
+    const int p0 = L.kgrp_ptr[grp];
+    const int nblk = L.kgrp_ptr[grp + 1] - p0;
     const float c2 = a.scale_log2;
     const bf16x8 zero8 = __builtin_bit_cast(bf16x8, (u32x4){0u, 0u, 0u, 0u});
 
-    auto issue = [&](int qb, unsigned char* qd, unsigned char* od, float* rd) {
+    auto issue = [&](int qb, int buf) {
         const unsigned short* Qt = Q + (int64_t)qb * T * D;
         const unsigned short* Ot = dO + (int64_t)qb * T * D;
 #pragma unroll
         for (int u = 0; u < NI; ++u) {
-            __builtin_amdgcn_global_load_lds((glb_void*)(Qt + goff[u]), (lds_void*)(qd + TL::load_dst(u, w)), 16, 0, 0);
-            __builtin_amdgcn_global_load_lds((glb_void*)(Ot + goff[u]), (lds_void*)(od + TL::load_dst(u, w)), 16, 0, 0);
+            __builtin_amdgcn_global_load_lds((glb_void*)(Qt + goff[u]), (lds_void*)(qbuf[buf] + TL::load_dst(u, w)), 16, 0, 0);
+            __builtin_amdgcn_global_load_lds((glb_void*)(Ot + goff[u]), (lds_void*)(obuf[buf] + TL::load_dst(u, w)), 16, 0, 0);
         }
-        const float* src = (w == 0 ? nl2g : dlg) + (int64_t)qb * T + lane;
-        __builtin_amdgcn_global_load_lds((glb_void*)src, (lds_void*)(rd + T * w), 4, 0, 0);
+        if (w < 2) {  // wave 0: nl2, wave 1: D
+            const float* src = (w == 0 ? nl2g : dlg) + (int64_t)qb * T + lane;
+            __builtin_amdgcn_global_load_lds((glb_void*)src, (lds_void*)(rbuf[buf] + T * w), 4, 0, 0);
+        }
     };
 
-    if (nblk > 0) issue(L.row_idx[p0], qbuf0, obuf0, rbuf0);
+    if (nblk > 0) issue(L.kgrp_step[p0].x, 0);
     wait_vmem();
     __syncthreads();
 
     for (int t = 0; t < nblk; ++t) {
-        const bool odd = t & 1;
-        const unsigned char* qc = odd ? qbuf1 : qbuf0;
-        const unsigned char* oc = odd ? obuf1 : obuf0;
-        const float* rc = odd ? rbuf1 : rbuf0;
-        if (t + 1 < nblk) issue(L.row_idx[p0 + t + 1], odd ? qbuf0 : qbuf1, odd ? obuf0 : obuf1, odd ? rbuf0 : rbuf1);
-        const int mid = L.col_mask[p0 + t];
-
-        f32x16 s[2], dp[2];
+        const int cur = t & 1;
+        const unsigned char* qc = qbuf[cur];
+        const unsigned char* oc = obuf[cur];
+        const float* rc = rbuf[cur];
+        if (t + 1 < nblk) issue(L.kgrp_step[p0 + t + 1].x, cur ^ 1);
+        const int4 step = L.kgrp_step[p0 + t];
+        const int mid = member ? step.z : step.y;  // -2: this key block is not listed
+        if (kb >= 0 && mid != -2) {
+            // Transposed lane-mask planes (set 0 for a full block, unused)
+            // first, then the liveness of each 32-query half.
+            const_u64* pl = (const_u64*)(L.planes_t + ((int64_t)(mid >= 0 ? mid : 0) * 2 + wr) * 32);
+            uint64_t pln[32];
 #pragma unroll
-        for (int qt = 0; qt < 2; ++qt) {
-            zero(s[qt]);
-            zero(dp[qt]);
-#pragma unroll
-            for (int c = 0; c < D / 16; ++c) {
-                const bf16x8 qa = *(const bf16x8*)(qc + aoff[c] + qt * 32 * TL::kRow);
-                const bf16x8 oa = *(const bf16x8*)(oc + aoff[c] + qt * 32 * TL::kRow);
-                s[qt] = mfma(qa, kop[c], s[qt]);
-                dp[qt] = mfma(oa, vop[c], dp[qt]);
-            }
-        }
-        // Masked elements get s = -inf, hence P = exp2(c2 s - lse log2 e) = 0 and
-        // dS = P (dP - D) = 0.  A 32-query half with no allowed element for
-        // this wave's keys has zero P and dS: its elementwise work is skipped,
-        // its products still run.
-        bool live[2] = {true, true};
-        if (mid >= 0) {
-            const_u64* pl = (const_u64*)(L.planes_t + ((int64_t)mid * 2 + w) * 32);
+            for (int r = 0; r < 32; ++r) pln[r] = pl[r];
+            bool live[2];
 #pragma unroll
             for (int qt = 0; qt < 2; ++qt) {
                 uint64_t any = 0;
 #pragma unroll
-                for (int i = 0; i < 16; ++i) any |= pl[16 * qt + i];
-                live[qt] = any != 0;
+                for (int i = 0; i < 16; ++i) any |= pln[16 * qt + i];
+                live[qt] = mid < 0 || any != 0;
+            }
+
+            f32x16 s[2], dp[2];
+            bf16x8 qa[2][D / 16], oa[2][D / 16];
+#pragma unroll
+            for (int qt = 0; qt < 2; ++qt)
+#pragma unroll
+                for (int c = 0; c < D / 16; ++c) {
+                    qa[qt][c] = *(const bf16x8*)(qc + aoff[c] + qt * 32 * TL::kRow);
+                    oa[qt][c] = *(const bf16x8*)(oc + aoff[c] + qt * 32 * TL::kRow);
+                }
+#pragma unroll
+            for (int qt = 0; qt < 2; ++qt) {
+                zero(s[qt]);
+                zero(dp[qt]);
+#pragma unroll
+                for (int c = 0; c < D / 16; ++c) {
+                    s[qt] = mfma(qa[qt][c], kop[c], s[qt]);
+                    dp[qt] = mfma(oa[qt][c], vop[c], dp[qt]);
+                }
+            }
+            // Per 32-query half: its operand reads, then its products.
+            __builtin_amdgcn_sched_group_barrier(0x100, D / 8, 0);
+            __builtin_amdgcn_sched_group_barrier(0x008, D / 8, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, D / 8, 0);
+            __builtin_amdgcn_sched_group_barrier(0x008, D / 8, 0);
+
+            // Masked elements get s = -inf, hence P = exp2(c2 s - lse log2 e)
+            // = 0 and dS = P (dP - D) = 0.  A 32-query half with no allowed
+            // element for this wave's keys skips its elementwise work; its
+            // products still run.
+            if (mid >= 0) {
+#pragma unroll
+                for (int qt = 0; qt < 2; ++qt)
+                    if (live[qt]) {
+#pragma unroll
+                        for (int i = 0; i < 16; ++i)
+                            s[qt][i] = __builtin_amdgcn_inverse_ballot_w64(pln[16 * qt + i]) ? s[qt][i] : -INFINITY;
+                    }
+            }
+#pragma unroll
+            for (int qt = 0; qt < 2; ++qt) {
+                bf16x8 ot[2][D / 32], qt8[2][D / 32];
+#pragma unroll
+                for (int h = 0; h < 2; ++h)
+#pragma unroll
+                    for (int dt = 0; dt < D / 32; ++dt) {
+                        const int cc = 2 * qt + h;
+                        ot[h][dt] = lds_read_tr8(oc + toff[0][dt] + cc * 16 * TL::kRow, oc + toff[1][dt] + cc * 16 * TL::kRow);
+                        qt8[h][dt] = lds_read_tr8(qc + toff[0][dt] + cc * 16 * TL::kRow, qc + toff[1][dt] + cc * 16 * TL::kRow);
+                    }
+                bf16x8 pb[2] = {zero8, zero8}, db[2] = {zero8, zero8};
                 if (live[qt]) {
 #pragma unroll
-                    for (int i = 0; i < 16; ++i)
-                        s[qt][i] = __builtin_amdgcn_inverse_ballot_w64(pl[16 * qt + i]) ? s[qt][i] : -INFINITY;
-                }
-            }
-        }
+                    for (int g = 0; g < 4; ++g) {
+                        const f32x4 nl = *(const f32x4*)&rc[32 * qt + 8 * g + 4 * hh];
+                        const f32x4 dd = *(const f32x4*)&rc[T + 32 * qt + 8 * g + 4 * hh];
 #pragma unroll
-        for (int qt = 0; qt < 2; ++qt) {
-            bf16x8 pb[2] = {zero8, zero8}, db[2] = {zero8, zero8};
-            if (live[qt]) {
-#pragma unroll
-                for (int g = 0; g < 4; ++g) {
-                    const f32x4 nl = *(const f32x4*)&rc[32 * qt + 8 * g + 4 * hh];
-                    const f32x4 dd = *(const f32x4*)&rc[T + 32 * qt + 8 * g + 4 * hh];
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        const int i = 4 * g + e;
-                        const float p = __builtin_amdgcn_exp2f(fmaf(s[qt][i], c2, nl[e]));
-                        s[qt][i] = p;
-                        dp[qt][i] = p * (dp[qt][i] - dd[e]);
+                        for (int e = 0; e < 4; ++e) {
+                            const int i = 4 * g + e;
+                            const float p = __builtin_amdgcn_exp2f(fmaf(s[qt][i], c2, nl[e]));
+                            s[qt][i] = p;
+                            dp[qt][i] = p * (dp[qt][i] - dd[e]);
+                        }
                     }
+                    pb[0] = pack8(s[qt], 0);
+                    pb[1] = pack8(s[qt], 8);
+                    db[0] = pack8(dp[qt], 0);
+                    db[1] = pack8(dp[qt], 8);
                 }
-                pb[0] = pack8(s[qt], 0);
-                pb[1] = pack8(s[qt], 8);
-                db[0] = pack8(dp[qt], 0);
-                db[1] = pack8(dp[qt], 8);
+#pragma unroll
+                for (int h = 0; h < 2; ++h)
+#pragma unroll
+                    for (int dt = 0; dt < D / 32; ++dt) {
+                        dv[dt] = mfma(ot[h][dt], pb[h], dv[dt]);
+                        dk[dt] = mfma(qt8[h][dt], db[h], dk[dt]);
+                    }
             }
-#pragma unroll
-            for (int h = 0; h < 2; ++h)
-#pragma unroll
-                for (int dt = 0; dt < D / 32; ++dt) {
-                    const int cc = 2 * qt + h;
-                    const bf16x8 ot = lds_read_tr8(oc + toff[0][dt] + cc * 16 * TL::kRow, oc + toff[1][dt] + cc * 16 * TL::kRow);
-                    const bf16x8 qt8 = lds_read_tr8(qc + toff[0][dt] + cc * 16 * TL::kRow, qc + toff[1][dt] + cc * 16 * TL::kRow);
-                    dv[dt] = mfma(ot, pb[h], dv[dt]);
-                    dk[dt] = mfma(qt8, db[h], dk[dt]);
-                }
-        }
+        }  // this wave's key block is listed by the query block
         wait_vmem();
         __syncthreads();
     }
 
+    if (kb < 0) return;
     // Register i of dk[dt]/dv[dt]: d = 32*dt + 8*(i/4) + 4*hh + i%4 of key k_row.
     unsigned short* DK = (unsigned short*)a.dk + head + k_row * D;
     unsigned short* DV = (unsigned short*)a.dv + head + k_row * D;
@@ -247,31 +285,36 @@ __global__ __launch_bounds__(128) void bwd_dkdv_kernel(const BwdArgs a)
 }
 
 // ---------------------------------------------------------------------------
-// dQ: workgroup = query block (bh, qb), wave w owns queries 32w..32w+31 and
-// walks the key blocks of the query block.  Lane (hh, n) holds query 32w + n.
+// dQ: workgroup = a pair of query blocks of one (batch, head) with nearly the
+// same key list (waves 0-1: rows of the first, waves 2-3: rows of the
+// second), walking the merged key list with shared, double-buffered K/V
+// tiles.  Lane (hh, n) of wave w holds query 32*(w%2) + n of its block.
 //   S^T  = K Q^T      C[key][q]  A = K rows (LDS)          B = Q^T (registers)
 //   dP^T = V dO^T     C[key][q]  A = V rows (LDS)          B = dO^T (registers)
 //   dQ^T += K^T dS^T  C[d][q]    A = K^T (transposing LDS read)  B = dS^T
 template <int D>
-__global__ __launch_bounds__(128) void bwd_dq_kernel(const BwdArgs a)
+__global__ __launch_bounds__(256) void bwd_dq_kernel(const BwdArgs a)
 {
     constexpr int T = 64;
-    typedef Tile64<D> TL;
-    constexpr int NI = TL::kBytes / 2048;
-    __shared__ __attribute__((aligned(1024))) unsigned char kbuf0[TL::kBytes], kbuf1[TL::kBytes];
-    __shared__ __attribute__((aligned(1024))) unsigned char vbuf0[TL::kBytes], vbuf1[TL::kBytes];
+    typedef Tile64<D, 4> TL;
+    constexpr int NI = TL::kLoads;
+    __shared__ __attribute__((aligned(1024))) unsigned char kbuf[2][TL::kBytes];
+    __shared__ __attribute__((aligned(1024))) unsigned char vbuf[2][TL::kBytes];
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int member = w >> 1, wr = w & 1;
     const int n32 = lane & 31, hh = lane >> 5;
     const Item item = a.items[blockIdx.x];
-    const int bh = item.bh, qb = item.blk;
+    const int bh = item.bh, grp = item.blk;
     const DevLayout L = a.heads.lay[a.heads.head_lay[bh % a.H]];
+    const int2 pair = L.qgrp_blk[grp];
+    const int qb = member ? pair.y : pair.x;  // -1: this wave has no rows
     const int64_t head = (int64_t)bh * a.n * D;
     const unsigned short* K = (const unsigned short*)a.k + head;
     const unsigned short* V = (const unsigned short*)a.v + head;
-    const int q_local = 32 * w + n32;
-    const int64_t q_row = (int64_t)qb * T + q_local;
+    const int q_local = 32 * wr + n32;
+    const int64_t q_row = (int64_t)(qb < 0 ? 0 : qb) * T + q_local;
 
     bf16x8 qop[D / 16], dop[D / 16];
     {
@@ -300,90 +343,117 @@ __global__ __launch_bounds__(128) void bwd_dq_kernel(const BwdArgs a)
     f32x16 dq[D / 32];
 #pragma unroll
     for (int dt = 0; dt < D / 32; ++dt) zero(dq[dt]);
-    const int p0 = L.row_ptr[qb];
-    const int nblk = L.row_ptr[qb + 1] - p0;
+    const int p0 = L.qgrp_ptr[grp];
+    const int nblk = L.qgrp_ptr[grp + 1] - p0;
     const float c2 = a.scale_log2;
     const bf16x8 zero8 = __builtin_bit_cast(bf16x8, (u32x4){0u, 0u, 0u, 0u});
 
-    auto issue = [&](int kb, unsigned char* kd, unsigned char* vd) {
+    auto issue = [&](int kb, int buf) {
         const unsigned short* Kt = K + (int64_t)kb * T * D;
         const unsigned short* Vt = V + (int64_t)kb * T * D;
 #pragma unroll
         for (int u = 0; u < NI; ++u) {
-            __builtin_amdgcn_global_load_lds((glb_void*)(Kt + goff[u]), (lds_void*)(kd + TL::load_dst(u, w)), 16, 0, 0);
-            __builtin_amdgcn_global_load_lds((glb_void*)(Vt + goff[u]), (lds_void*)(vd + TL::load_dst(u, w)), 16, 0, 0);
+            __builtin_amdgcn_global_load_lds((glb_void*)(Kt + goff[u]), (lds_void*)(kbuf[buf] + TL::load_dst(u, w)), 16, 0, 0);
+            __builtin_amdgcn_global_load_lds((glb_void*)(Vt + goff[u]), (lds_void*)(vbuf[buf] + TL::load_dst(u, w)), 16, 0, 0);
         }
     };
 
-    if (nblk > 0) issue(L.col_idx[p0], kbuf0, vbuf0);
+    if (nblk > 0) issue(L.qgrp_step[p0].x, 0);
     wait_vmem();
     __syncthreads();
 
     for (int t = 0; t < nblk; ++t) {
-        const bool odd = t & 1;
-        const unsigned char* kc = odd ? kbuf1 : kbuf0;
-        const unsigned char* vc = odd ? vbuf1 : vbuf0;
-        if (t + 1 < nblk) issue(L.col_idx[p0 + t + 1], odd ? kbuf0 : kbuf1, odd ? vbuf0 : vbuf1);
-        const int mid = L.mask_id[p0 + t];
-
-        f32x16 s[2], dp[2];
+        const int cur = t & 1;
+        const unsigned char* kc = kbuf[cur];
+        const unsigned char* vc = vbuf[cur];
+        if (t + 1 < nblk) issue(L.qgrp_step[p0 + t + 1].x, cur ^ 1);
+        const int4 step = L.qgrp_step[p0 + t];
+        const int mid = member ? step.z : step.y;  // -2: not in this block's list
+        if (qb >= 0 && mid != -2) {
+            // Lane-mask planes (set 0 for a full block, unused) first, so the
+            // scalar loads overlap the products; then the liveness of each
+            // 32-key half.
+            const_u64* pl = (const_u64*)(L.planes + ((int64_t)(mid >= 0 ? mid : 0) * 2 + wr) * 32);
+            uint64_t pln[32];
 #pragma unroll
-        for (int kt = 0; kt < 2; ++kt) {
-            zero(s[kt]);
-            zero(dp[kt]);
-#pragma unroll
-            for (int c = 0; c < D / 16; ++c) {
-                const bf16x8 ka = *(const bf16x8*)(kc + aoff[c] + kt * 32 * TL::kRow);
-                const bf16x8 va = *(const bf16x8*)(vc + aoff[c] + kt * 32 * TL::kRow);
-                s[kt] = mfma(ka, qop[c], s[kt]);
-                dp[kt] = mfma(va, dop[c], dp[kt]);
-            }
-        }
-        // Register i of tile kt: key 32*kt + 8*(i/4) + 4*hh + i%4 of query
-        // q_local.  Masked elements get s = -inf, so P^T and dS^T = P^T (dP^T -
-        // D) are zero there; a 32-key half with no allowed element for this
-        // wave's queries is skipped.
-        bool live[2] = {true, true};
-        if (mid >= 0) {
-            const_u64* pl = (const_u64*)(L.planes + ((int64_t)mid * 2 + w) * 32);
+            for (int r = 0; r < 32; ++r) pln[r] = pl[r];
+            bool live[2];
 #pragma unroll
             for (int kt = 0; kt < 2; ++kt) {
                 uint64_t any = 0;
 #pragma unroll
-                for (int i = 0; i < 16; ++i) any |= pl[16 * kt + i];
-                live[kt] = any != 0;
+                for (int i = 0; i < 16; ++i) any |= pln[16 * kt + i];
+                live[kt] = mid < 0 || any != 0;
+            }
+
+            f32x16 s[2], dp[2];
+            bf16x8 ka[2][D / 16], va[2][D / 16];
+#pragma unroll
+            for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+                for (int c = 0; c < D / 16; ++c) {
+                    ka[kt][c] = *(const bf16x8*)(kc + aoff[c] + kt * 32 * TL::kRow);
+                    va[kt][c] = *(const bf16x8*)(vc + aoff[c] + kt * 32 * TL::kRow);
+                }
+#pragma unroll
+            for (int kt = 0; kt < 2; ++kt) {
+                zero(s[kt]);
+                zero(dp[kt]);
+#pragma unroll
+                for (int c = 0; c < D / 16; ++c) {
+                    s[kt] = mfma(ka[kt][c], qop[c], s[kt]);
+                    dp[kt] = mfma(va[kt][c], dop[c], dp[kt]);
+                }
+            }
+            // Per 32-key half: its 2*D/16 operand reads, then its products.
+            __builtin_amdgcn_sched_group_barrier(0x100, D / 8, 0);  // LDS reads
+            __builtin_amdgcn_sched_group_barrier(0x008, D / 8, 0);  // MFMA
+            __builtin_amdgcn_sched_group_barrier(0x100, D / 8, 0);
+            __builtin_amdgcn_sched_group_barrier(0x008, D / 8, 0);
+
+            // Register i of tile kt: key 32*kt + 8*(i/4) + 4*hh + i%4 of query
+            // q_local.  Masked elements get s = -inf, so P^T and dS^T = P^T
+            // (dP^T - D) are zero there; a dead 32-key half skips this work.
+            if (mid >= 0) {
+#pragma unroll
+                for (int kt = 0; kt < 2; ++kt)
+                    if (live[kt]) {
+#pragma unroll
+                        for (int i = 0; i < 16; ++i)
+                            s[kt][i] = __builtin_amdgcn_inverse_ballot_w64(pln[16 * kt + i]) ? s[kt][i] : -INFINITY;
+                    }
+            }
+#pragma unroll
+            for (int kt = 0; kt < 2; ++kt) {
+                bf16x8 kop[2][D / 32];
+#pragma unroll
+                for (int h = 0; h < 2; ++h)
+#pragma unroll
+                    for (int dt = 0; dt < D / 32; ++dt) {
+                        const int cc = 2 * kt + h;
+                        kop[h][dt] = lds_read_tr8(kc + toff[0][dt] + cc * 16 * TL::kRow, kc + toff[1][dt] + cc * 16 * TL::kRow);
+                    }
+                bf16x8 db[2] = {zero8, zero8};
                 if (live[kt]) {
 #pragma unroll
-                    for (int i = 0; i < 16; ++i)
-                        s[kt][i] = __builtin_amdgcn_inverse_ballot_w64(pl[16 * kt + i]) ? s[kt][i] : -INFINITY;
+                    for (int i = 0; i < 16; ++i) {
+                        const float p = __builtin_amdgcn_exp2f(fmaf(s[kt][i], c2, nl2));
+                        dp[kt][i] = p * (dp[kt][i] - d_i);
+                    }
+                    db[0] = pack8(dp[kt], 0);
+                    db[1] = pack8(dp[kt], 8);
                 }
+#pragma unroll
+                for (int h = 0; h < 2; ++h)
+#pragma unroll
+                    for (int dt = 0; dt < D / 32; ++dt) dq[dt] = mfma(kop[h][dt], db[h], dq[dt]);
             }
-        }
-#pragma unroll
-        for (int kt = 0; kt < 2; ++kt) {
-            bf16x8 db[2] = {zero8, zero8};
-            if (live[kt]) {
-#pragma unroll
-                for (int i = 0; i < 16; ++i) {
-                    const float p = __builtin_amdgcn_exp2f(fmaf(s[kt][i], c2, nl2));
-                    dp[kt][i] = p * (dp[kt][i] - d_i);
-                }
-                db[0] = pack8(dp[kt], 0);
-                db[1] = pack8(dp[kt], 8);
-            }
-#pragma unroll
-            for (int h = 0; h < 2; ++h)
-#pragma unroll
-                for (int dt = 0; dt < D / 32; ++dt) {
-                    const int cc = 2 * kt + h;
-                    const bf16x8 kt8 = lds_read_tr8(kc + toff[0][dt] + cc * 16 * TL::kRow, kc + toff[1][dt] + cc * 16 * TL::kRow);
-                    dq[dt] = mfma(kt8, db[h], dq[dt]);
-                }
-        }
+        }  // this wave's block lists the key block
         wait_vmem();
         __syncthreads();
     }
 
+    if (qb < 0) return;
     unsigned short* DQ = (unsigned short*)a.dq + head + q_row * D;
 #pragma unroll
     for (int dt = 0; dt < D / 32; ++dt)
@@ -412,18 +482,18 @@ hipError_t launch_bwd_rowterms_bf16(int d, const BwdArgs& a, int64_t rows, hipSt
 hipError_t launch_bwd_dkdv_bf16_t64(int d, const BwdArgs& a, int n_items, hipStream_t stream)
 {
     if (d == 64)
-        hipLaunchKernelGGL(bwd_dkdv_kernel<64>, dim3(n_items), dim3(128), 0, stream, a);
+        hipLaunchKernelGGL(bwd_dkdv_kernel<64>, dim3(n_items), dim3(256), 0, stream, a);
     else
-        hipLaunchKernelGGL(bwd_dkdv_kernel<128>, dim3(n_items), dim3(128), 0, stream, a);
+        hipLaunchKernelGGL(bwd_dkdv_kernel<128>, dim3(n_items), dim3(256), 0, stream, a);
     return hipGetLastError();
 }
 
 hipError_t launch_bwd_dq_bf16_t64(int d, const BwdArgs& a, int n_items, hipStream_t stream)
 {
     if (d == 64)
-        hipLaunchKernelGGL(bwd_dq_kernel<64>, dim3(n_items), dim3(128), 0, stream, a);
+        hipLaunchKernelGGL(bwd_dq_kernel<64>, dim3(n_items), dim3(256), 0, stream, a);
     else
-        hipLaunchKernelGGL(bwd_dq_kernel<128>, dim3(n_items), dim3(128), 0, stream, a);
+        hipLaunchKernelGGL(bwd_dq_kernel<128>, dim3(n_items), dim3(256), 0, stream, a);
     return hipGetLastError();
 }
 

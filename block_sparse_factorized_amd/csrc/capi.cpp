@@ -161,10 +161,10 @@ int device_layout(sa_layout* L, int dev, DevLayout* out)
 }
 
 // ---------------------------------------------------------------------------
-// Work lists.  One item per (batch*head, block); ordered longest first so the
+// Work lists.  One item per (batch*head, block or block pair); ordered longest first so the
 // heaviest blocks start early and the tail is made of short ones.  Cached per
 // (kind, device, B, H, layouts).
-enum ListKind { kByQuery = 0, kByKey = 1, kByQueryPair = 2 };
+enum ListKind { kByQuery = 0, kByQueryPair = 1, kByKeyPair = 2 };
 
 struct Plan {
     Item* items;
@@ -186,7 +186,11 @@ int get_plan(ListKind kind, int dev, int32_t B, int32_t H, sa_layout* const* hl,
         return SA_OK;
     }
     auto listing = [&](const sa_layout* L) -> const std::vector<int32_t>& {
-        return kind == kByQuery ? L->row_ptr : kind == kByKey ? L->col_ptr : L->qgroups.ptr;
+        switch (kind) {
+        case kByQuery: return L->row_ptr;
+        case kByQueryPair: return L->qgroups.ptr;
+        default: return L->kgroups.ptr;
+        }
     };
     int64_t count = 0;
     for (int32_t bh = 0; bh < B * H; ++bh) count += (int64_t)listing(hl[bh % H]).size() - 1;
@@ -420,11 +424,11 @@ int bwd_call(const char* fn, int stages, const sa_layout_t* const* head_layout, 
     if (st != SA_OK) return st;
     Plan pk{nullptr, 0}, pq{nullptr, 0};
     if (kv) {
-        st = get_plan(kByKey, dev, B, H, hl.data(), &pk);
+        st = get_plan(kByKeyPair, dev, B, H, hl.data(), &pk);
         if (st != SA_OK) return st;
     }
     if (dqs) {
-        st = get_plan(kByQuery, dev, B, H, hl.data(), &pq);
+        st = get_plan(kByQueryPair, dev, B, H, hl.data(), &pq);
         if (st != SA_OK) return st;
     }
     BwdArgs a;

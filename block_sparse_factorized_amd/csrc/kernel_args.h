@@ -9,8 +9,10 @@
 
 namespace sa {
 
-// One (batch*H + head, block) work item; y is a query block for the forward
-// and dQ kernels and a key block for the dK/dV kernel.
+// One (batch*H + head, block) work item.  blk is a query block for the fp32
+// forward kernel, and an index into the layout's pair lists (query-block
+// pairs for the bf16 forward and dQ kernels, key-block pairs for the dK/dV
+// kernel) otherwise.
 struct Item {
     int32_t bh;
     int32_t blk;
