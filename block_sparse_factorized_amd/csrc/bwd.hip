@@ -22,7 +22,9 @@
 // sequence axis are read with the transposing LDS load, the sequence index of
 // each 16-long reduction chunk is taken in the order {0-3, 8-11} (lanes 0-31)
 // and {4-7, 12-15} (lanes 32-63) so that accumulator registers feed the next
-// MFMA directly, and partial-block masks are 64-bit lane masks in SGPRs.
+// MFMA directly, partial-block masks are 64-bit lane masks in SGPRs, and a
+// 32 x 32 quadrant of a block with no allowed element is skipped (it would
+// only add zeros).
 #include <hip/hip_runtime.h>
 
 #include "kernel_args.h"
@@ -89,18 +91,24 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(const BwdArgs a)
     constexpr int T = 64;
     typedef Tile64<D, 4> TL;
     constexpr int NI = TL::kLoads;
-    __shared__ __attribute__((aligned(1024))) unsigned char qbuf[2][TL::kBytes];
-    __shared__ __attribute__((aligned(1024))) unsigned char obuf[2][TL::kBytes];
-    __shared__ __attribute__((aligned(16))) float rbuf[2][2 * T];  // nl2[64], then D[64]
+    // Two sets of Q/dO/row-term buffers as separate objects, used alternately
+    // by a loop unrolled by two, so that the LDS reads of the current tile
+    // are seen not to depend on the loads in flight to the other set.
+    __shared__ __attribute__((aligned(1024))) unsigned char qbuf0[TL::kBytes];
+    __shared__ __attribute__((aligned(1024))) unsigned char obuf0[TL::kBytes];
+    __shared__ __attribute__((aligned(1024))) unsigned char qbuf1[TL::kBytes];
+    __shared__ __attribute__((aligned(1024))) unsigned char obuf1[TL::kBytes];
+    __shared__ __attribute__((aligned(16))) float rbuf0[2 * T];  // nl2[64], then D[64]
+    __shared__ __attribute__((aligned(16))) float rbuf1[2 * T];
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int member = w >> 1, wr = w & 1;
     const int n32 = lane & 31, hh = lane >> 5;
-    const Item item = a.items[blockIdx.x];
+    const Item item = ld_uniform(&a.items[blockIdx.x]);
     const int bh = item.bh, grp = item.blk;
     const DevLayout L = a.heads.lay[a.heads.head_lay[bh % a.H]];
-    const int2 pair = L.kgrp_blk[grp];
+    const int2 pair = ld_uniform(&L.kgrp_blk[grp]);
     const int kb = member ? pair.y : pair.x;  // -1: this wave has no keys
     const int64_t head = (int64_t)bh * a.n * D;
     const unsigned short* Q = (const unsigned short*)a.q + head;
@@ -138,104 +146,80 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(const BwdArgs a)
         zero(dk[dt]);
         zero(dv[dt]);
     }
-    const int p0 = L.kgrp_ptr[grp];
-    const int nblk = L.kgrp_ptr[grp + 1] - p0;
+    const int p0 = ld_uniform(&L.kgrp_ptr[grp]);
+    const int nblk = ld_uniform(&L.kgrp_ptr[grp + 1]) - p0;
     const float c2 = a.scale_log2;
-    const bf16x8 zero8 = __builtin_bit_cast(bf16x8, (u32x4){0u, 0u, 0u, 0u});
 
-    auto issue = [&](int qb, int buf) {
+    auto issue = [&](int qb, unsigned char* qd, unsigned char* od, float* rd) {
         const unsigned short* Qt = Q + (int64_t)qb * T * D;
         const unsigned short* Ot = dO + (int64_t)qb * T * D;
 #pragma unroll
         for (int u = 0; u < NI; ++u) {
-            __builtin_amdgcn_global_load_lds((glb_void*)(Qt + goff[u]), (lds_void*)(qbuf[buf] + TL::load_dst(u, w)), 16, 0, 0);
-            __builtin_amdgcn_global_load_lds((glb_void*)(Ot + goff[u]), (lds_void*)(obuf[buf] + TL::load_dst(u, w)), 16, 0, 0);
+            __builtin_amdgcn_global_load_lds((glb_void*)(Qt + goff[u]), (lds_void*)(qd + TL::load_dst(u, w)), 16, 0, 0);
+            __builtin_amdgcn_global_load_lds((glb_void*)(Ot + goff[u]), (lds_void*)(od + TL::load_dst(u, w)), 16, 0, 0);
         }
         if (w < 2) {  // wave 0: nl2, wave 1: D
             const float* src = (w == 0 ? nl2g : dlg) + (int64_t)qb * T + lane;
-            __builtin_amdgcn_global_load_lds((glb_void*)src, (lds_void*)(rbuf[buf] + T * w), 4, 0, 0);
+            __builtin_amdgcn_global_load_lds((glb_void*)src, (lds_void*)(rd + T * w), 4, 0, 0);
         }
     };
 
-    if (nblk > 0) issue(L.kgrp_step[p0].x, 0);
-    wait_vmem();
-    __syncthreads();
-
-    for (int t = 0; t < nblk; ++t) {
-        const int cur = t & 1;
-        const unsigned char* qc = qbuf[cur];
-        const unsigned char* oc = obuf[cur];
-        const float* rc = rbuf[cur];
-        if (t + 1 < nblk) issue(L.kgrp_step[p0 + t + 1].x, cur ^ 1);
-        const int4 step = L.kgrp_step[p0 + t];
+    // One step: start the next tile's loads into (qn, on, rn), accumulate the
+    // tile in (qc, oc, rc), then wait for the next tile.
+    auto step_tile = [&](int t, const unsigned char* qc, const unsigned char* oc, const float* rc,
+                         unsigned char* qn, unsigned char* on, float* rn) {
+        if (t + 1 < nblk) issue(ld_uniform(&L.kgrp_step[p0 + t + 1]).x, qn, on, rn);
+        const int4 step = ld_uniform(&L.kgrp_step[p0 + t]);
         const int mid = member ? step.z : step.y;  // -2: this key block is not listed
         if (kb >= 0 && mid != -2) {
-            // Transposed lane-mask planes (set 0 for a full block, unused)
-            // first, then the liveness of each 32-query half.
+            // Transposed lane-mask planes (set 0 for a full block, unused),
+            // loaded before the products so the scalar loads overlap them.
+            // A 32-query half is live when the mask has an allowed element in
+            // quadrant (query half qt, key half wr).
             const_u64* pl = (const_u64*)(L.planes_t + ((int64_t)(mid >= 0 ? mid : 0) * 2 + wr) * 32);
             uint64_t pln[32];
 #pragma unroll
             for (int r = 0; r < 32; ++r) pln[r] = pl[r];
+            const unsigned quad = (unsigned)step.w >> (4 * member);
             bool live[2];
 #pragma unroll
-            for (int qt = 0; qt < 2; ++qt) {
-                uint64_t any = 0;
-#pragma unroll
-                for (int i = 0; i < 16; ++i) any |= pln[16 * qt + i];
-                live[qt] = mid < 0 || any != 0;
-            }
+            for (int qt = 0; qt < 2; ++qt) live[qt] = (quad >> (2 * qt + wr)) & 1u;
 
-            f32x16 s[2], dp[2];
-            bf16x8 qa[2][D / 16], oa[2][D / 16];
+            // One 32-query half at a time; a half with no allowed element for
+            // this wave's keys is skipped entirely (it would only add zeros).
+            // Masked elements get s = -inf, hence P = exp2(c2 s - lse log2 e)
+            // = 0 and dS = P (dP - D) = 0.
 #pragma unroll
             for (int qt = 0; qt < 2; ++qt)
+                if (live[qt]) {
+                    f32x16 s, dp;
+                    bf16x8 qa[D / 16], oa[D / 16];
 #pragma unroll
-                for (int c = 0; c < D / 16; ++c) {
-                    qa[qt][c] = *(const bf16x8*)(qc + aoff[c] + qt * 32 * TL::kRow);
-                    oa[qt][c] = *(const bf16x8*)(oc + aoff[c] + qt * 32 * TL::kRow);
-                }
+                    for (int c = 0; c < D / 16; ++c) {
+                        qa[c] = *(const bf16x8*)(qc + aoff[c] + qt * 32 * TL::kRow);
+                        oa[c] = *(const bf16x8*)(oc + aoff[c] + qt * 32 * TL::kRow);
+                    }
+                    zero(s);
+                    zero(dp);
 #pragma unroll
-            for (int qt = 0; qt < 2; ++qt) {
-                zero(s[qt]);
-                zero(dp[qt]);
-#pragma unroll
-                for (int c = 0; c < D / 16; ++c) {
-                    s[qt] = mfma(qa[qt][c], kop[c], s[qt]);
-                    dp[qt] = mfma(oa[qt][c], vop[c], dp[qt]);
-                }
-            }
-            // Per 32-query half: its operand reads, then its products.
-            __builtin_amdgcn_sched_group_barrier(0x100, D / 8, 0);
-            __builtin_amdgcn_sched_group_barrier(0x008, D / 8, 0);
-            __builtin_amdgcn_sched_group_barrier(0x100, D / 8, 0);
-            __builtin_amdgcn_sched_group_barrier(0x008, D / 8, 0);
-
-            // Masked elements get s = -inf, hence P = exp2(c2 s - lse log2 e)
-            // = 0 and dS = P (dP - D) = 0.  A 32-query half with no allowed
-            // element for this wave's keys skips its elementwise work; its
-            // products still run.
-            if (mid >= 0) {
-#pragma unroll
-                for (int qt = 0; qt < 2; ++qt)
-                    if (live[qt]) {
+                    for (int c = 0; c < D / 16; ++c) {
+                        s = mfma(qa[c], kop[c], s);
+                        dp = mfma(oa[c], vop[c], dp);
+                    }
+                    if (mid >= 0) {
 #pragma unroll
                         for (int i = 0; i < 16; ++i)
-                            s[qt][i] = __builtin_amdgcn_inverse_ballot_w64(pln[16 * qt + i]) ? s[qt][i] : -INFINITY;
+                            s[i] = __builtin_amdgcn_inverse_ballot_w64(pln[16 * qt + i]) ? s[i] : -INFINITY;
                     }
-            }
+                    bf16x8 ot[2][D / 32], qt8[2][D / 32];
 #pragma unroll
-            for (int qt = 0; qt < 2; ++qt) {
-                bf16x8 ot[2][D / 32], qt8[2][D / 32];
+                    for (int h = 0; h < 2; ++h)
 #pragma unroll
-                for (int h = 0; h < 2; ++h)
-#pragma unroll
-                    for (int dt = 0; dt < D / 32; ++dt) {
-                        const int cc = 2 * qt + h;
-                        ot[h][dt] = lds_read_tr8(oc + toff[0][dt] + cc * 16 * TL::kRow, oc + toff[1][dt] + cc * 16 * TL::kRow);
-                        qt8[h][dt] = lds_read_tr8(qc + toff[0][dt] + cc * 16 * TL::kRow, qc + toff[1][dt] + cc * 16 * TL::kRow);
-                    }
-                bf16x8 pb[2] = {zero8, zero8}, db[2] = {zero8, zero8};
-                if (live[qt]) {
+                        for (int dt = 0; dt < D / 32; ++dt) {
+                            const int cc = 2 * qt + h;
+                            ot[h][dt] = lds_read_tr8(oc + toff[0][dt] + cc * 16 * TL::kRow, oc + toff[1][dt] + cc * 16 * TL::kRow);
+                            qt8[h][dt] = lds_read_tr8(qc + toff[0][dt] + cc * 16 * TL::kRow, qc + toff[1][dt] + cc * 16 * TL::kRow);
+                        }
 #pragma unroll
                     for (int g = 0; g < 4; ++g) {
                         const f32x4 nl = *(const f32x4*)&rc[32 * qt + 8 * g + 4 * hh];
@@ -243,27 +227,32 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(const BwdArgs a)
 #pragma unroll
                         for (int e = 0; e < 4; ++e) {
                             const int i = 4 * g + e;
-                            const float p = __builtin_amdgcn_exp2f(fmaf(s[qt][i], c2, nl[e]));
-                            s[qt][i] = p;
-                            dp[qt][i] = p * (dp[qt][i] - dd[e]);
+                            const float p = __builtin_amdgcn_exp2f(fmaf(s[i], c2, nl[e]));
+                            s[i] = p;
+                            dp[i] = p * (dp[i] - dd[e]);
                         }
                     }
-                    pb[0] = pack8(s[qt], 0);
-                    pb[1] = pack8(s[qt], 8);
-                    db[0] = pack8(dp[qt], 0);
-                    db[1] = pack8(dp[qt], 8);
+                    const bf16x8 pb[2] = {pack8(s, 0), pack8(s, 8)};
+                    const bf16x8 db[2] = {pack8(dp, 0), pack8(dp, 8)};
+#pragma unroll
+                    for (int h = 0; h < 2; ++h)
+#pragma unroll
+                        for (int dt = 0; dt < D / 32; ++dt) {
+                            dv[dt] = mfma(ot[h][dt], pb[h], dv[dt]);
+                            dk[dt] = mfma(qt8[h][dt], db[h], dk[dt]);
+                        }
                 }
-#pragma unroll
-                for (int h = 0; h < 2; ++h)
-#pragma unroll
-                    for (int dt = 0; dt < D / 32; ++dt) {
-                        dv[dt] = mfma(ot[h][dt], pb[h], dv[dt]);
-                        dk[dt] = mfma(qt8[h][dt], db[h], dk[dt]);
-                    }
-            }
         }  // this wave's key block is listed by the query block
         wait_vmem();
         __syncthreads();
+    };
+
+    if (nblk > 0) issue(ld_uniform(&L.kgrp_step[p0]).x, qbuf0, obuf0, rbuf0);
+    wait_vmem();
+    __syncthreads();
+    for (int t = 0; t < nblk; t += 2) {
+        step_tile(t, qbuf0, obuf0, rbuf0, qbuf1, obuf1, rbuf1);
+        if (t + 1 < nblk) step_tile(t + 1, qbuf1, obuf1, rbuf1, qbuf0, obuf0, rbuf0);
     }
 
     if (kb < 0) return;
@@ -292,23 +281,30 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(const BwdArgs a)
 //   S^T  = K Q^T      C[key][q]  A = K rows (LDS)          B = Q^T (registers)
 //   dP^T = V dO^T     C[key][q]  A = V rows (LDS)          B = dO^T (registers)
 //   dQ^T += K^T dS^T  C[d][q]    A = K^T (transposing LDS read)  B = dS^T
+// With d = 64 the kernel fits four waves per SIMD (its only spill is of a
+// value used after the loop).
 template <int D>
-__global__ __launch_bounds__(256) void bwd_dq_kernel(const BwdArgs a)
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D == 64 ? 4 : 1))) void bwd_dq_kernel(
+    const BwdArgs a)
 {
     constexpr int T = 64;
     typedef Tile64<D, 4> TL;
     constexpr int NI = TL::kLoads;
-    __shared__ __attribute__((aligned(1024))) unsigned char kbuf[2][TL::kBytes];
-    __shared__ __attribute__((aligned(1024))) unsigned char vbuf[2][TL::kBytes];
+    // Two K/V buffer pairs as separate objects, used alternately by a loop
+    // unrolled by two (see the dK/dV kernel).
+    __shared__ __attribute__((aligned(1024))) unsigned char kbuf0[TL::kBytes];
+    __shared__ __attribute__((aligned(1024))) unsigned char vbuf0[TL::kBytes];
+    __shared__ __attribute__((aligned(1024))) unsigned char kbuf1[TL::kBytes];
+    __shared__ __attribute__((aligned(1024))) unsigned char vbuf1[TL::kBytes];
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int member = w >> 1, wr = w & 1;
     const int n32 = lane & 31, hh = lane >> 5;
-    const Item item = a.items[blockIdx.x];
+    const Item item = ld_uniform(&a.items[blockIdx.x]);
     const int bh = item.bh, grp = item.blk;
     const DevLayout L = a.heads.lay[a.heads.head_lay[bh % a.H]];
-    const int2 pair = L.qgrp_blk[grp];
+    const int2 pair = ld_uniform(&L.qgrp_blk[grp]);
     const int qb = member ? pair.y : pair.x;  // -1: this wave has no rows
     const int64_t head = (int64_t)bh * a.n * D;
     const unsigned short* K = (const unsigned short*)a.k + head;
@@ -343,114 +339,98 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(const BwdArgs a)
     f32x16 dq[D / 32];
 #pragma unroll
     for (int dt = 0; dt < D / 32; ++dt) zero(dq[dt]);
-    const int p0 = L.qgrp_ptr[grp];
-    const int nblk = L.qgrp_ptr[grp + 1] - p0;
+    const int p0 = ld_uniform(&L.qgrp_ptr[grp]);
+    const int nblk = ld_uniform(&L.qgrp_ptr[grp + 1]) - p0;
     const float c2 = a.scale_log2;
-    const bf16x8 zero8 = __builtin_bit_cast(bf16x8, (u32x4){0u, 0u, 0u, 0u});
 
-    auto issue = [&](int kb, int buf) {
+    auto issue = [&](int kb, unsigned char* kd, unsigned char* vd) {
         const unsigned short* Kt = K + (int64_t)kb * T * D;
         const unsigned short* Vt = V + (int64_t)kb * T * D;
 #pragma unroll
         for (int u = 0; u < NI; ++u) {
-            __builtin_amdgcn_global_load_lds((glb_void*)(Kt + goff[u]), (lds_void*)(kbuf[buf] + TL::load_dst(u, w)), 16, 0, 0);
-            __builtin_amdgcn_global_load_lds((glb_void*)(Vt + goff[u]), (lds_void*)(vbuf[buf] + TL::load_dst(u, w)), 16, 0, 0);
+            __builtin_amdgcn_global_load_lds((glb_void*)(Kt + goff[u]), (lds_void*)(kd + TL::load_dst(u, w)), 16, 0, 0);
+            __builtin_amdgcn_global_load_lds((glb_void*)(Vt + goff[u]), (lds_void*)(vd + TL::load_dst(u, w)), 16, 0, 0);
         }
     };
 
-    if (nblk > 0) issue(L.qgrp_step[p0].x, 0);
-    wait_vmem();
-    __syncthreads();
-
-    for (int t = 0; t < nblk; ++t) {
-        const int cur = t & 1;
-        const unsigned char* kc = kbuf[cur];
-        const unsigned char* vc = vbuf[cur];
-        if (t + 1 < nblk) issue(L.qgrp_step[p0 + t + 1].x, cur ^ 1);
-        const int4 step = L.qgrp_step[p0 + t];
+    // One step: start the next tile's loads into (kn, vn), accumulate the
+    // tile in (kc, vc), then wait for the next tile.
+    auto step_tile = [&](int t, const unsigned char* kc, const unsigned char* vc, unsigned char* kn,
+                         unsigned char* vn) {
+        if (t + 1 < nblk) issue(ld_uniform(&L.qgrp_step[p0 + t + 1]).x, kn, vn);
+        const int4 step = ld_uniform(&L.qgrp_step[p0 + t]);
         const int mid = member ? step.z : step.y;  // -2: not in this block's list
         if (qb >= 0 && mid != -2) {
             // Lane-mask planes (set 0 for a full block, unused) first, so the
-            // scalar loads overlap the products; then the liveness of each
-            // 32-key half.
+            // scalar loads overlap the products.  A 32-key half is live when
+            // the mask has an allowed element in quadrant (query half wr, key
+            // half kt).
             const_u64* pl = (const_u64*)(L.planes + ((int64_t)(mid >= 0 ? mid : 0) * 2 + wr) * 32);
             uint64_t pln[32];
 #pragma unroll
             for (int r = 0; r < 32; ++r) pln[r] = pl[r];
+            const unsigned quad = (unsigned)step.w >> (4 * member);
             bool live[2];
 #pragma unroll
-            for (int kt = 0; kt < 2; ++kt) {
-                uint64_t any = 0;
-#pragma unroll
-                for (int i = 0; i < 16; ++i) any |= pln[16 * kt + i];
-                live[kt] = mid < 0 || any != 0;
-            }
+            for (int kt = 0; kt < 2; ++kt) live[kt] = (quad >> (2 * wr + kt)) & 1u;
 
-            f32x16 s[2], dp[2];
-            bf16x8 ka[2][D / 16], va[2][D / 16];
+            // One 32-key half at a time; a half with no allowed element for
+            // this wave's rows is skipped entirely (it would only add zeros).
+            // Register i of a half's tile: key 32*kt + 8*(i/4) + 4*hh + i%4
+            // of query q_local.  Masked elements get s = -inf, so P^T and
+            // dS^T = P^T (dP^T - D) are zero there.
 #pragma unroll
             for (int kt = 0; kt < 2; ++kt)
+                if (live[kt]) {
+                    f32x16 s, dp;
+                    bf16x8 ka[D / 16], va[D / 16];
 #pragma unroll
-                for (int c = 0; c < D / 16; ++c) {
-                    ka[kt][c] = *(const bf16x8*)(kc + aoff[c] + kt * 32 * TL::kRow);
-                    va[kt][c] = *(const bf16x8*)(vc + aoff[c] + kt * 32 * TL::kRow);
-                }
+                    for (int c = 0; c < D / 16; ++c) {
+                        ka[c] = *(const bf16x8*)(kc + aoff[c] + kt * 32 * TL::kRow);
+                        va[c] = *(const bf16x8*)(vc + aoff[c] + kt * 32 * TL::kRow);
+                    }
+                    zero(s);
+                    zero(dp);
 #pragma unroll
-            for (int kt = 0; kt < 2; ++kt) {
-                zero(s[kt]);
-                zero(dp[kt]);
-#pragma unroll
-                for (int c = 0; c < D / 16; ++c) {
-                    s[kt] = mfma(ka[kt][c], qop[c], s[kt]);
-                    dp[kt] = mfma(va[kt][c], dop[c], dp[kt]);
-                }
-            }
-            // Per 32-key half: its 2*D/16 operand reads, then its products.
-            __builtin_amdgcn_sched_group_barrier(0x100, D / 8, 0);  // LDS reads
-            __builtin_amdgcn_sched_group_barrier(0x008, D / 8, 0);  // MFMA
-            __builtin_amdgcn_sched_group_barrier(0x100, D / 8, 0);
-            __builtin_amdgcn_sched_group_barrier(0x008, D / 8, 0);
-
-            // Register i of tile kt: key 32*kt + 8*(i/4) + 4*hh + i%4 of query
-            // q_local.  Masked elements get s = -inf, so P^T and dS^T = P^T
-            // (dP^T - D) are zero there; a dead 32-key half skips this work.
-            if (mid >= 0) {
-#pragma unroll
-                for (int kt = 0; kt < 2; ++kt)
-                    if (live[kt]) {
+                    for (int c = 0; c < D / 16; ++c) {
+                        s = mfma(ka[c], qop[c], s);
+                        dp = mfma(va[c], dop[c], dp);
+                    }
+                    if (mid >= 0) {
 #pragma unroll
                         for (int i = 0; i < 16; ++i)
-                            s[kt][i] = __builtin_amdgcn_inverse_ballot_w64(pln[16 * kt + i]) ? s[kt][i] : -INFINITY;
+                            s[i] = __builtin_amdgcn_inverse_ballot_w64(pln[16 * kt + i]) ? s[i] : -INFINITY;
                     }
-            }
+                    bf16x8 kop[2][D / 32];
 #pragma unroll
-            for (int kt = 0; kt < 2; ++kt) {
-                bf16x8 kop[2][D / 32];
+                    for (int h = 0; h < 2; ++h)
 #pragma unroll
-                for (int h = 0; h < 2; ++h)
-#pragma unroll
-                    for (int dt = 0; dt < D / 32; ++dt) {
-                        const int cc = 2 * kt + h;
-                        kop[h][dt] = lds_read_tr8(kc + toff[0][dt] + cc * 16 * TL::kRow, kc + toff[1][dt] + cc * 16 * TL::kRow);
-                    }
-                bf16x8 db[2] = {zero8, zero8};
-                if (live[kt]) {
+                        for (int dt = 0; dt < D / 32; ++dt) {
+                            const int cc = 2 * kt + h;
+                            kop[h][dt] = lds_read_tr8(kc + toff[0][dt] + cc * 16 * TL::kRow, kc + toff[1][dt] + cc * 16 * TL::kRow);
+                        }
 #pragma unroll
                     for (int i = 0; i < 16; ++i) {
-                        const float p = __builtin_amdgcn_exp2f(fmaf(s[kt][i], c2, nl2));
-                        dp[kt][i] = p * (dp[kt][i] - d_i);
+                        const float p = __builtin_amdgcn_exp2f(fmaf(s[i], c2, nl2));
+                        dp[i] = p * (dp[i] - d_i);
                     }
-                    db[0] = pack8(dp[kt], 0);
-                    db[1] = pack8(dp[kt], 8);
+                    const bf16x8 db[2] = {pack8(dp, 0), pack8(dp, 8)};
+#pragma unroll
+                    for (int h = 0; h < 2; ++h)
+#pragma unroll
+                        for (int dt = 0; dt < D / 32; ++dt) dq[dt] = mfma(kop[h][dt], db[h], dq[dt]);
                 }
-#pragma unroll
-                for (int h = 0; h < 2; ++h)
-#pragma unroll
-                    for (int dt = 0; dt < D / 32; ++dt) dq[dt] = mfma(kop[h][dt], db[h], dq[dt]);
-            }
         }  // this wave's block lists the key block
         wait_vmem();
         __syncthreads();
+    };
+
+    if (nblk > 0) issue(ld_uniform(&L.qgrp_step[p0]).x, kbuf0, vbuf0);
+    wait_vmem();
+    __syncthreads();
+    for (int t = 0; t < nblk; t += 2) {
+        step_tile(t, kbuf0, vbuf0, kbuf1, vbuf1);
+        if (t + 1 < nblk) step_tile(t + 1, kbuf1, vbuf1, kbuf0, vbuf0);
     }
 
     if (qb < 0) return;

@@ -123,10 +123,26 @@ int device_layout(sa_layout* L, int dev, DevLayout* out)
         memcpy(&host[off_col_mask], col_mask.data(), nnz * 4);
     }
     memcpy(&host[off_col_ptr], L->col_ptr.data(), nqb1 * 4);
+    // Quadrant occupancy of every mask (block size 64): bit 2*rh + ch.
+    std::vector<uint8_t> quad((size_t)L->n_masks, 0);
+    if (L->T == 64)
+        for (int64_t m = 0; m < L->n_masks; ++m)
+            for (int r = 0; r < 64; ++r) {
+                const uint64_t row = L->masks[m * 64 + r];  // query row r: bit s = key s
+                if (row & 0x00000000ffffffffull) quad[m] |= (uint8_t)(1u << (2 * (r / 32)));
+                if (row & 0xffffffff00000000ull) quad[m] |= (uint8_t)(1u << (2 * (r / 32) + 1));
+            }
+    auto quad_of = [&](int32_t m) -> uint32_t { return m == -1 ? 0xFu : m == -2 ? 0u : quad[m]; };
     for (int k = 0; k < 2; ++k) {
         memcpy(&host[off_gptr[k]], gs[k]->ptr.data(), gs[k]->ptr.size() * 4);
         if (!gs[k]->blk.empty()) memcpy(&host[off_gblk[k]], gs[k]->blk.data(), gs[k]->blk.size() * 4);
-        if (!gs[k]->step.empty()) memcpy(&host[off_gstep[k]], gs[k]->step.data(), gs[k]->step.size() * 4);
+        int32_t* st = (int32_t*)&host[off_gstep[k]];
+        for (size_t x = 0; x < gs[k]->step.size(); x += 4) {
+            st[x] = gs[k]->step[x];
+            st[x + 1] = gs[k]->step[x + 1];
+            st[x + 2] = gs[k]->step[x + 2];
+            st[x + 3] = (int32_t)(quad_of(st[x + 1]) | quad_of(st[x + 2]) << 4);
+        }
     }
     void* mem = nullptr;
     hipError_t e = hipMalloc(&mem, total);

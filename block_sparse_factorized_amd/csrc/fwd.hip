@@ -10,8 +10,10 @@
 // Only O and lse leave the kernel; no score matrix is stored ("[논문 리뷰]
 // Generating Long Sequences with Sparse Transformers", ABSTRACT (b)).
 //
-// bf16 kernel (block 64, d in {64, 128}), one workgroup of two waves per
-// (batch, head, query block); wave w owns query rows 32w..32w+31.
+// bf16 kernel (block 64, d in {64, 128}), one workgroup of four waves per
+// pair of query blocks of one (batch, head) whose key lists (nearly)
+// coincide; waves 2m and 2m+1 own query rows 0..31 and 32..63 of member m,
+// and the K/V tiles of the merged list are loaded once for both members.
 //   * The score tile is computed transposed, S^T = K Q^T, with
 //     v_mfma_f32_32x32x16_bf16: lane (hh = lane/32, n = lane%32) then holds
 //     16 keys of query n per 32-key half, so the row max and row sum are
@@ -24,14 +26,16 @@
 //     V^T operand comes straight from the row-major V tile through the
 //     transposing LDS read (ds_read_b64_tr_b16).
 //   * K and V tiles go from HBM straight into LDS (global_load_lds_dwordx4)
-//     in a bank-conflict-free swizzled layout.  With d = 64 a single buffer
-//     is used: keeping LDS per workgroup small lets four waves per SIMD
-//     hide the load latency, which measured faster than double buffering.
+//     in a bank-conflict-free swizzled layout, double buffered: the next
+//     tile's loads run under the current tile's work.
 //   * Partial blocks are masked with 64-bit lane masks held in SGPRs (one
-//     v_cndmask per element); a 32-key half with no allowed element for the
-//     wave skips its softmax work (its products still run, on zero weights).
+//     v_cndmask per element).  A 32 x 32 quadrant of the block (this wave's
+//     32 rows, one 32-key half) with no allowed element is skipped: no score
+//     products, softmax or output products for it.
 //   * The running max is moved only when a row's max grows by more than
 //     2^8 in the exponent, so the accumulator rescale is rare.
+//   * Work-list metadata is read with scalar loads, so waiting for it never
+//     waits for tiles in flight.
 //
 // f32 kernel (block 16, d 64), one wave per (batch, head, query block), the
 // same transposed structure on v_mfma_f32_16x16x4_f32.
@@ -43,15 +47,20 @@
 namespace sa {
 namespace {
 
-template <int D, int NBUF>
+template <int D>
 __global__ __launch_bounds__(256) void fwd_bf16_t64_kernel(const FwdArgs a)
 {
     constexpr int T = 64;
     typedef Tile64<D, 4> TL;
     constexpr int NI = TL::kLoads;  // direct-to-LDS loads per wave per tensor
-    constexpr int PD = NBUF > 1 ? NBUF - 1 : 0;  // tiles loaded ahead of the one in use
-    __shared__ __attribute__((aligned(1024))) unsigned char kbuf[NBUF][TL::kBytes];
-    __shared__ __attribute__((aligned(1024))) unsigned char vbuf[NBUF][TL::kBytes];
+    // Two K/V buffers as separate objects: the loop below is unrolled by two
+    // so that every step reads one buffer and fills the other with statically
+    // known addresses, which lets the compiler see that the LDS reads of the
+    // current tile do not wait for the tile in flight to the other buffer.
+    __shared__ __attribute__((aligned(1024))) unsigned char kbuf0[TL::kBytes];
+    __shared__ __attribute__((aligned(1024))) unsigned char vbuf0[TL::kBytes];
+    __shared__ __attribute__((aligned(1024))) unsigned char kbuf1[TL::kBytes];
+    __shared__ __attribute__((aligned(1024))) unsigned char vbuf1[TL::kBytes];
 
     // Work item: a pair of query blocks of one (batch, head) with nearly the
     // same key list; waves 0-1 own the rows of the first block, waves 2-3 the
@@ -60,10 +69,10 @@ __global__ __launch_bounds__(256) void fwd_bf16_t64_kernel(const FwdArgs a)
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int member = w >> 1, wr = w & 1;
     const int n32 = lane & 31, hh = lane >> 5;
-    const Item item = a.items[blockIdx.x];
+    const Item item = ld_uniform(&a.items[blockIdx.x]);
     const int bh = item.bh, grp = item.blk;
     const DevLayout L = a.heads.lay[a.heads.head_lay[bh % a.H]];
-    const int2 pair = L.qgrp_blk[grp];
+    const int2 pair = ld_uniform(&L.qgrp_blk[grp]);
     const int qb = member ? pair.y : pair.x;  // -1: this wave has no rows
     const int64_t head = (int64_t)bh * a.n * D;
     const unsigned short* Q = (const unsigned short*)a.q + head;
@@ -91,8 +100,8 @@ __global__ __launch_bounds__(256) void fwd_bf16_t64_kernel(const FwdArgs a)
 #pragma unroll
         for (int dt = 0; dt < D / 32; ++dt) voff[j4][dt] = TL::tr_off(lane, j4, dt);
 
-    const int p0 = L.qgrp_ptr[grp];
-    const int nblk = L.qgrp_ptr[grp + 1] - p0;
+    const int p0 = ld_uniform(&L.qgrp_ptr[grp]);
+    const int nblk = ld_uniform(&L.qgrp_ptr[grp + 1]) - p0;
 
     f32x16 oacc[D / 32];
 #pragma unroll
@@ -101,156 +110,132 @@ __global__ __launch_bounds__(256) void fwd_bf16_t64_kernel(const FwdArgs a)
         for (int i = 0; i < 16; ++i) oacc[dt][i] = 0.f;
     float m_ref = -INFINITY, l_run = 0.f;
     const float c2 = a.scale_log2;
-    const bf16x8 zero8 = __builtin_bit_cast(bf16x8, (u32x4){0u, 0u, 0u, 0u});
 
-    auto issue = [&](int kb, int buf) {
+    auto issue = [&](int kb, unsigned char* kd, unsigned char* vd) {
         const unsigned short* Kt = K + (int64_t)kb * T * D;
         const unsigned short* Vt = V + (int64_t)kb * T * D;
 #pragma unroll
         for (int u = 0; u < NI; ++u) {
-            __builtin_amdgcn_global_load_lds((glb_void*)(Kt + goff[u]), (lds_void*)(kbuf[buf] + TL::load_dst(u, w)), 16, 0, 0);
-            __builtin_amdgcn_global_load_lds((glb_void*)(Vt + goff[u]), (lds_void*)(vbuf[buf] + TL::load_dst(u, w)), 16, 0, 0);
+            __builtin_amdgcn_global_load_lds((glb_void*)(Kt + goff[u]), (lds_void*)(kd + TL::load_dst(u, w)), 16, 0, 0);
+            __builtin_amdgcn_global_load_lds((glb_void*)(Vt + goff[u]), (lds_void*)(vd + TL::load_dst(u, w)), 16, 0, 0);
         }
     };
 
-    // Prologue: the first PD tiles (one tile when single-buffered).
-#pragma unroll
-    for (int pre = 0; pre < (PD > 0 ? PD : 1); ++pre)
-        if (pre < nblk) issue(L.qgrp_step[p0 + pre].x, pre);
-    wait_vmem();
-    __syncthreads();
-
-    int cur = 0;
-    for (int t = 0; t < nblk; ++t) {
-        const unsigned char* kc = kbuf[cur];
-        const unsigned char* vc = vbuf[cur];
-        if (PD > 0 && t + PD < nblk) issue(L.qgrp_step[p0 + t + PD].x, (cur + PD) % NBUF);
-        const int4 step = L.qgrp_step[p0 + t];
+    // One step: start the loads of tile t + 1 into (kn, vn), fold the tile
+    // in (kc, vc) into the online softmax, then wait for tile t + 1.
+    auto step_tile = [&](int t, const unsigned char* kc, const unsigned char* vc, unsigned char* kn,
+                         unsigned char* vn) {
+        if (t + 1 < nblk) issue(ld_uniform(&L.qgrp_step[p0 + t + 1]).x, kn, vn);
+        const int4 step = ld_uniform(&L.qgrp_step[p0 + t]);
         const int mid = member ? step.z : step.y;  // -2: not in this block's list
         if (qb >= 0 && mid != -2) {
+            // Lane masks of every score register, one 64-bit plane each, loaded
+            // into SGPRs before the products so the loads overlap them (a full
+            // block reads plane set 0, unused).  The constant address space lets
+            // these wave-uniform loads be scalar loads.
+            const_u64* pl = (const_u64*)(L.planes + ((int64_t)(mid >= 0 ? mid : 0) * 2 + wr) * 32);
+            uint64_t pln[32];
+#pragma unroll
+            for (int r = 0; r < 32; ++r) pln[r] = pl[r];
+            // A 32-key half with no allowed element in this wave's rows (quadrant
+            // (query half wr, key half kt) of the mask empty) has only zero
+            // weights: its scores, softmax and products are skipped, since they
+            // would only add zeros to the output.
+            const unsigned quad = (unsigned)step.w >> (4 * member);
+            bool live[2];
+#pragma unroll
+            for (int kt = 0; kt < 2; ++kt) live[kt] = (quad >> (2 * wr + kt)) & 1u;
 
-        // Lane masks of every score register, one 64-bit plane each, loaded
-        // into SGPRs before the products so the loads overlap them (a full
-        // block reads plane set 0, unused).  The constant address space lets
-        // these wave-uniform loads be scalar loads.
-        const_u64* pl = (const_u64*)(L.planes + ((int64_t)(mid >= 0 ? mid : 0) * 2 + wr) * 32);
-        uint64_t pln[32];
+            // S^T = K Q^T: register i of s[kt] holds key 32*kt + 8*(i/4) + 4*hh + i%4 of query n.
+            // A live half's operand reads first, then its products.
+            f32x16 s[2];
 #pragma unroll
-        for (int r = 0; r < 32; ++r) pln[r] = pl[r];
-        // A 32-key half with no allowed element in this wave's rows (all 16 of
-        // its planes zero) has only zero weights, so its softmax work is
-        // skipped; its matrix products still run, with zero weights.
-        bool live[2];
+            for (int kt = 0; kt < 2; ++kt)
+                if (live[kt]) {
+                    bf16x8 kop[D / 16];
 #pragma unroll
-        for (int kt = 0; kt < 2; ++kt) {
-            uint64_t any = 0;
+                    for (int c = 0; c < D / 16; ++c) kop[c] = *(const bf16x8*)(kc + koff[c] + kt * 32 * TL::kRow);
 #pragma unroll
-            for (int i = 0; i < 16; ++i) any |= pln[16 * kt + i];
-            live[kt] = mid < 0 || any != 0;
-        }
+                    for (int i = 0; i < 16; ++i) s[kt][i] = 0.f;
+#pragma unroll
+                    for (int c = 0; c < D / 16; ++c)
+                        s[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop[c], qop[c], s[kt], 0, 0, 0);
+                }
 
-        // S^T = K Q^T: register i of s[kt] holds key 32*kt + 8*(i/4) + 4*hh + i%4 of query n.
-        // All operand reads first, then the products.
-        f32x16 s[2];
-        bf16x8 kop[2][D / 16];
+            // Partial block: disallowed elements to -inf.
+            if (mid >= 0) {
 #pragma unroll
-        for (int kt = 0; kt < 2; ++kt)
+                for (int kt = 0; kt < 2; ++kt)
+                    if (live[kt]) {
 #pragma unroll
-            for (int c = 0; c < D / 16; ++c) kop[kt][c] = *(const bf16x8*)(kc + koff[c] + kt * 32 * TL::kRow);
-#pragma unroll
-        for (int kt = 0; kt < 2; ++kt) {
-#pragma unroll
-            for (int i = 0; i < 16; ++i) s[kt][i] = 0.f;
-#pragma unroll
-            for (int c = 0; c < D / 16; ++c)
-                s[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop[kt][c], qop[c], s[kt], 0, 0, 0);
-        }
-        __builtin_amdgcn_sched_group_barrier(0x100, D / 8, 0);  // LDS reads
-        __builtin_amdgcn_sched_group_barrier(0x008, D / 8, 0);  // MFMA
-
-        // Partial block: disallowed elements to -inf.
-        if (mid >= 0) {
+                        for (int i = 0; i < 16; ++i)
+                            s[kt][i] = __builtin_amdgcn_inverse_ballot_w64(pln[16 * kt + i]) ? s[kt][i] : -INFINITY;
+                    }
+            }
+            float mx = -INFINITY;
 #pragma unroll
             for (int kt = 0; kt < 2; ++kt)
                 if (live[kt]) {
 #pragma unroll
-                    for (int i = 0; i < 16; ++i)
-                        s[kt][i] = __builtin_amdgcn_inverse_ballot_w64(pln[16 * kt + i]) ? s[kt][i] : -INFINITY;
+                    for (int i = 0; i < 16; ++i) mx = __builtin_fmaxf(mx, s[kt][i]);
                 }
-        }
-        float mx = -INFINITY;
-#pragma unroll
-        for (int kt = 0; kt < 2; ++kt)
-            if (live[kt]) {
-#pragma unroll
-                for (int i = 0; i < 16; ++i) mx = __builtin_fmaxf(mx, s[kt][i]);
-            }
-        mx = half_max(mx);
+            mx = half_max(mx);
 
-        // Lazy rescale: keep the reference max unless some row's max grew by more
-        // than 2^8 in the exponent (then every lane of the wave rescales).
-        const float m_new = __builtin_fmaxf(m_ref, mx);
-        if (__builtin_amdgcn_ballot_w64((m_new - m_ref) * c2 > 8.f)) {
-            const float alpha = m_new == -INFINITY ? 1.f : __builtin_amdgcn_exp2f((m_ref - m_new) * c2);
-            l_run *= alpha;
-#pragma unroll
-            for (int dt = 0; dt < D / 32; ++dt)
-#pragma unroll
-                for (int i = 0; i < 16; ++i) oacc[dt][i] *= alpha;
-            m_ref = m_new;
-        }
-        const float mc = m_ref == -INFINITY ? 0.f : m_ref * c2;
-
-        // P^T (chunk cc of P^T is registers 8*(cc%2)..+7 of s[cc/2]), then
-        // O^T += V^T P^T, one 32-key half at a time; the half's V^T operands
-        // are read before its exponentials so the LDS latency overlaps them.
-#pragma unroll
-        for (int kt = 0; kt < 2; ++kt) {
-            bf16x8 vop[2][D / 32];
-#pragma unroll
-            for (int h = 0; h < 2; ++h)
-#pragma unroll
-                for (int dt = 0; dt < D / 32; ++dt) {
-                    const int cc = 2 * kt + h;
-                    vop[h][dt] = lds_read_tr8(vc + voff[0][dt] + cc * 16 * TL::kRow,
-                                              vc + voff[1][dt] + cc * 16 * TL::kRow);
-                }
-            bf16x8 pb[2] = {zero8, zero8};
-            if (live[kt]) {
-                float lsum = 0.f;
-#pragma unroll
-                for (int i = 0; i < 16; ++i) {
-                    const float p = __builtin_amdgcn_exp2f(fmaf(s[kt][i], c2, -mc));
-                    s[kt][i] = p;
-                    lsum += p;
-                }
-                l_run += lsum;
-                pb[0] = pack8(s[kt], 0);
-                pb[1] = pack8(s[kt], 8);
-            }
-#pragma unroll
-            for (int h = 0; h < 2; ++h)
+            // Lazy rescale: keep the reference max unless some row's max grew by
+            // more than 2^8 in the exponent (then every lane of the wave rescales).
+            const float m_new = __builtin_fmaxf(m_ref, mx);
+            if (__builtin_amdgcn_ballot_w64((m_new - m_ref) * c2 > 8.f)) {
+                const float alpha = m_new == -INFINITY ? 1.f : __builtin_amdgcn_exp2f((m_ref - m_new) * c2);
+                l_run *= alpha;
 #pragma unroll
                 for (int dt = 0; dt < D / 32; ++dt)
-                    oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop[h][dt], pb[h], oacc[dt], 0, 0, 0);
-        }
+#pragma unroll
+                    for (int i = 0; i < 16; ++i) oacc[dt][i] *= alpha;
+                m_ref = m_new;
+            }
+            const float mc = m_ref == -INFINITY ? 0.f : m_ref * c2;
 
+            // P^T (chunk cc of P^T is registers 8*(cc%2)..+7 of s[cc/2]), then
+            // O^T += V^T P^T, one 32-key half at a time; the half's V^T operands
+            // are read before its exponentials so the LDS latency overlaps them.
+#pragma unroll
+            for (int kt = 0; kt < 2; ++kt)
+                if (live[kt]) {
+                    bf16x8 vop[2][D / 32];
+#pragma unroll
+                    for (int h = 0; h < 2; ++h)
+#pragma unroll
+                        for (int dt = 0; dt < D / 32; ++dt) {
+                            const int cc = 2 * kt + h;
+                            vop[h][dt] = lds_read_tr8(vc + voff[0][dt] + cc * 16 * TL::kRow,
+                                                      vc + voff[1][dt] + cc * 16 * TL::kRow);
+                        }
+                    float lsum = 0.f;
+#pragma unroll
+                    for (int i = 0; i < 16; ++i) {
+                        const float p = __builtin_amdgcn_exp2f(fmaf(s[kt][i], c2, -mc));
+                        s[kt][i] = p;
+                        lsum += p;
+                    }
+                    l_run += lsum;
+                    const bf16x8 pb[2] = {pack8(s[kt], 0), pack8(s[kt], 8)};
+#pragma unroll
+                    for (int h = 0; h < 2; ++h)
+#pragma unroll
+                        for (int dt = 0; dt < D / 32; ++dt)
+                            oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop[h][dt], pb[h], oacc[dt], 0, 0, 0);
+                }
         }  // this wave's block lists the key block
+        wait_vmem();      // tile t + 1 has landed ...
+        __syncthreads();  // ... for every wave, and every wave is done with tile t
+    };
 
-        if constexpr (PD == 0) {
-            __syncthreads();  // every wave is done with the only buffer
-            if (t + 1 < nblk) issue(L.qgrp_step[p0 + t + 1].x, 0);
-            wait_vmem();
-        } else if constexpr (PD >= 2) {
-            if (t + PD < nblk)
-                wait_vmcnt<2 * NI * (PD - 1)>();  // tile t+1 landed; later ones may still fly
-            else
-                wait_vmem();
-        } else {
-            wait_vmem();
-        }
-        __syncthreads();
-        cur = (cur + 1 == NBUF) ? 0 : cur + 1;
+    if (nblk > 0) issue(ld_uniform(&L.qgrp_step[p0]).x, kbuf0, vbuf0);
+    wait_vmem();
+    __syncthreads();
+    for (int t = 0; t < nblk; t += 2) {
+        step_tile(t, kbuf0, vbuf0, kbuf1, vbuf1);
+        if (t + 1 < nblk) step_tile(t + 1, kbuf1, vbuf1, kbuf0, vbuf0);
     }
 
     if (qb < 0) return;
@@ -365,13 +350,10 @@ __global__ __launch_bounds__(64) void fwd_f32_t16_d64_kernel(const FwdArgs a)
 
 hipError_t launch_fwd_bf16_t64(int d, const FwdArgs& a, int n_items, hipStream_t stream)
 {
-#ifndef SA_FWD_NBUF
-#define SA_FWD_NBUF 2
-#endif
     if (d == 64)
-        hipLaunchKernelGGL((fwd_bf16_t64_kernel<64, SA_FWD_NBUF>), dim3(n_items), dim3(256), 0, stream, a);
+        hipLaunchKernelGGL(fwd_bf16_t64_kernel<64>, dim3(n_items), dim3(256), 0, stream, a);
     else
-        hipLaunchKernelGGL((fwd_bf16_t64_kernel<128, 2>), dim3(n_items), dim3(256), 0, stream, a);
+        hipLaunchKernelGGL(fwd_bf16_t64_kernel<128>, dim3(n_items), dim3(256), 0, stream, a);
     return hipGetLastError();
 }
 

@@ -39,8 +39,11 @@ struct DevLayout {
     // workgroup (qgrp: query blocks over their key lists; kgrp: key blocks
     // over their query lists).  Group g has members grp_blk[g] = {a, b}
     // (b = -1 for a single block) and steps grp_ptr[g] .. grp_ptr[g+1]-1;
-    // step = {other block, mask of a, mask of b, 0}, mask -1 = full block,
-    // -2 = that member does not list this block.
+    // step = {other block, mask of a, mask of b, quadrants}, mask -1 = full
+    // block, -2 = that member does not list this block.  quadrants: bits 0-3
+    // for a, 4-7 for b; bit 2*rh + ch is set when the member's mask has an
+    // allowed element with query row in half rh and key in half ch of the
+    // 64 x 64 block (all four for a full block, none for -2).
     const int32_t* qgrp_ptr;
     const int2* qgrp_blk;
     const int4* qgrp_step;

@@ -23,6 +23,23 @@ typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(4))) const uint64_t const_u64;
 typedef __attribute__((address_space(4))) const int32_t const_i32;
 
+// Read-only, wave-uniform data read through the constant address space, so
+// that it becomes a scalar load: scalar loads are counted by lgkmcnt, and a
+// wait for them does not also wait for tiles in flight to LDS (vmcnt).
+// The value is read as 32-bit words (the HIP vector types' copy constructors
+// would take a generic reference and turn it back into a vector load).
+template <class T>
+__device__ static inline T ld_uniform(const T* p)
+{
+    static_assert(sizeof(T) % 4 == 0, "ld_uniform reads whole 32-bit words");
+    int32_t w[sizeof(T) / 4];
+#pragma unroll
+    for (unsigned i = 0; i < sizeof(T) / 4; ++i) w[i] = ((const_i32*)p)[i];
+    T r;
+    __builtin_memcpy(&r, w, sizeof(T));
+    return r;
+}
+
 __device__ static inline unsigned bf16_pair(float x, float y)
 {
     return __builtin_bit_cast(unsigned, __builtin_convertvector((f32x2){x, y}, bf16x2));

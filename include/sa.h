@@ -175,9 +175,11 @@ int sa_bwd(const sa_layout_t* const* head_layout, int32_t B, int32_t H, int64_t 
  *   sa_bwd_rowterms  the row terms D_i = sum_t dO_it O_it and -lse_i log2(e)
  *                    into the workspace
  *   sa_bwd_dkdv      dK, dV (reads the row terms from the workspace), one
- *                    workgroup per key block walking its query blocks
+ *                    workgroup per pair of key blocks walking their query
+ *                    blocks
  *   sa_bwd_dq        dQ (reads the row terms from the workspace), one
- *                    workgroup per query block walking its key blocks
+ *                    workgroup per pair of query blocks walking their key
+ *                    blocks
  * sa_bwd_dkdv and sa_bwd_dq must be ordered after sa_bwd_rowterms on the
  * device.  Same errors as sa_bwd.
  */
