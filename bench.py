@@ -79,6 +79,31 @@ def counted_flops(layouts, batch, T, d):
     return blocks * 4.0 * T * T * d, blocks
 
 
+def live_quadrants(layouts, batch, T):
+    """32 x 32 quadrants of the listed blocks that hold an allowed element,
+    summed over (batch, head).  The block-64 kernels skip the others, so
+    their matrix cores execute this many quadrants' products; the counted
+    metric charges four quadrants for every listed block."""
+    import numpy as np
+    total = 0
+    for lay in layouts:
+        ex = lay.export()
+        mid = np.asarray(ex["mask_id"])
+        if T != 64:  # only block-64 kernels skip quadrants
+            total += 4 * len(mid)
+            continue
+        words = np.asarray(ex["mask_words"]).reshape(-1, 64)  # row r of a mask = word r
+        if len(words):
+            lo = (words & np.uint64(0xFFFFFFFF)) != 0
+            hi = (words >> np.uint64(32)) != 0
+            per_mask = (lo[:, :32].any(1).astype(np.int64) + hi[:, :32].any(1) + lo[:, 32:].any(1)
+                        + hi[:, 32:].any(1))
+            total += int(np.where(mid < 0, 4, per_mask[np.maximum(mid, 0)]).sum())
+        else:
+            total += 4 * len(mid)
+    return total * batch
+
+
 def cpu_baseline(w, x, pats, T, max_heads):
     """The fp64 oracle on the host's cores over a bounded sample of heads of
     the same workload, fwd + bwd, scaled to the same counted-flop metric."""
@@ -194,12 +219,19 @@ def main():
     # backward 10*T*T*d split as dK/dV 8*T*T*d (S, dP, dV, dK) and dQ 2*T*T*d
     # (dQ itself; the S and dP it recomputes are not counted twice).
     per_block = {"fwd": 4.0, "bwd_dkdv": 8.0, "bwd_dq": 2.0, "bwd_rowterms": 0.0}
+    # Matrix-core flops the kernels execute, per live 32 x 32 quadrant
+    # (forward S, PV; dK/dV S, dP, dV, dK; dQ S, dP, dQ).
+    # The fp32 block-16 kernel skips nothing: it executes what is counted.
+    quads = live_quadrants(lays, w.batch, T)
+    per_quad = {"fwd": 4.0, "bwd_dkdv": 8.0, "bwd_dq": 6.0, "bwd_rowterms": 0.0}
     kernels = {}
     for nm in names:
         avg_s = float(kernel_ms[nm].mean()) * 1e-3
         fl = per_block[nm] * T * T * d * blocks
+        ex = per_quad[nm] * 32 * 32 * d * quads if T == 64 else fl
         kernels[nm] = {"avg_us": avg_s * 1e6, "median_us": float(np.median(kernel_ms[nm])) * 1e3,
-                       "counted_gflop": fl / 1e9, "tflops": fl / avg_s / 1e12 if fl else None}
+                       "counted_gflop": fl / 1e9, "tflops": fl / avg_s / 1e12 if fl else None,
+                       "executed_gflop": ex / 1e9, "executed_tflops": ex / avg_s / 1e12 if ex else None}
     dominant = max(names, key=lambda nm: kernels[nm]["avg_us"])
     kern_sym = {
         "fwd": "fwd_bf16_t64_kernel<%d>" % d if w.dtype == "bf16" else "fwd_f32_t16_d64_kernel",
@@ -219,6 +251,9 @@ def main():
         "traffic": traffic_from_profile(kern_file, kern_sym[dominant], w.name + ("-dense" if args.dense else "")),
         "counted_flops_per_launch": dk_["counted_gflop"] * 1e9,
         "avg_launch_us": dk_["avg_us"],
+        # What the matrix cores actually execute (empty quadrants skipped).
+        "executed_mfma_tflops": dk_["executed_tflops"],
+        "executed_frac": dk_["executed_tflops"] / peak,
     }
     out = {
         "metric": METRIC,
@@ -240,6 +275,7 @@ def main():
             "scale": scale, "allowed_blocks": blocks, "backward": w.backward,
         },
         "frac_of_peak": value / peak,
+        "live_quadrant_fraction": quads / (4.0 * blocks) if blocks else None,
         "kernels": kernels,
         "fwd_frac_of_peak": kernels["fwd"]["tflops"] / peak,
         "layout_build_ms": layout_ms,
@@ -247,7 +283,7 @@ def main():
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:
-        heads = args.cpu_heads or {"tiny": 2, "img32": 16, "text": 16, "img64": 24, "audio": 2}[w.name]
+        heads = args.cpu_heads or {"tiny": 2, "img32": 16, "text": 16, "img64": 32, "audio": 2}[w.name]
         out["cpu_baseline"] = cpu_baseline(w, x, pats, T, heads)
     print(json.dumps(out), flush=True)
 
