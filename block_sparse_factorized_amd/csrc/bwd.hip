@@ -128,9 +128,10 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(const BwdArgs a)
             vop[c] = *(const bf16x8*)(V + 16 * c + 8 * hh);
         }
     }
-    int goff[NI];
+    // (byte offsets from the tile's first element)
+    uint32_t goff[NI];
 #pragma unroll
-    for (int u = 0; u < NI; ++u) goff[u] = TL::load_src(u, w, lane);
+    for (int u = 0; u < NI; ++u) goff[u] = 2u * (uint32_t)TL::load_src(u, w, lane);
     int aoff[D / 16];
 #pragma unroll
     for (int c = 0; c < D / 16; ++c) aoff[c] = TL::off(n32, 2 * c + hh);
@@ -155,8 +156,8 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(const BwdArgs a)
         const unsigned short* Ot = dO + (int64_t)qb * T * D;
 #pragma unroll
         for (int u = 0; u < NI; ++u) {
-            __builtin_amdgcn_global_load_lds((glb_void*)(Qt + goff[u]), (lds_void*)(qd + TL::load_dst(u, w)), 16, 0, 0);
-            __builtin_amdgcn_global_load_lds((glb_void*)(Ot + goff[u]), (lds_void*)(od + TL::load_dst(u, w)), 16, 0, 0);
+            __builtin_amdgcn_global_load_lds((glb_void*)sgpr_base_plus(Qt, goff[u]), (lds_void*)(qd + TL::load_dst(u, w)), 16, 0, 0);
+            __builtin_amdgcn_global_load_lds((glb_void*)sgpr_base_plus(Ot, goff[u]), (lds_void*)(od + TL::load_dst(u, w)), 16, 0, 0);
         }
         if (w < 2) {  // wave 0: nl2, wave 1: D
             const float* src = (w == 0 ? nl2g : dlg) + (int64_t)qb * T + lane;
@@ -324,9 +325,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D == 64 ? 4
     }
     const float nl2 = a.nl2[(int64_t)bh * a.n + q_row];
     const float d_i = a.delta[(int64_t)bh * a.n + q_row];
-    int goff[NI];
+    // (byte offsets from the tile's first element)
+    uint32_t goff[NI];
 #pragma unroll
-    for (int u = 0; u < NI; ++u) goff[u] = TL::load_src(u, w, lane);
+    for (int u = 0; u < NI; ++u) goff[u] = 2u * (uint32_t)TL::load_src(u, w, lane);
     int aoff[D / 16];
 #pragma unroll
     for (int c = 0; c < D / 16; ++c) aoff[c] = TL::off(n32, 2 * c + hh);
@@ -348,8 +350,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D == 64 ? 4
         const unsigned short* Vt = V + (int64_t)kb * T * D;
 #pragma unroll
         for (int u = 0; u < NI; ++u) {
-            __builtin_amdgcn_global_load_lds((glb_void*)(Kt + goff[u]), (lds_void*)(kd + TL::load_dst(u, w)), 16, 0, 0);
-            __builtin_amdgcn_global_load_lds((glb_void*)(Vt + goff[u]), (lds_void*)(vd + TL::load_dst(u, w)), 16, 0, 0);
+            __builtin_amdgcn_global_load_lds((glb_void*)sgpr_base_plus(Kt, goff[u]), (lds_void*)(kd + TL::load_dst(u, w)), 16, 0, 0);
+            __builtin_amdgcn_global_load_lds((glb_void*)sgpr_base_plus(Vt, goff[u]), (lds_void*)(vd + TL::load_dst(u, w)), 16, 0, 0);
         }
     };
 

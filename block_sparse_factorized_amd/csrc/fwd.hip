@@ -87,9 +87,10 @@ __global__ __launch_bounds__(256) void fwd_bf16_t64_kernel(const FwdArgs a)
     for (int c = 0; c < D / 16; ++c) qop[c] = *(const bf16x8*)(Q + q_row * D + 16 * c + 8 * hh);
 
     // Per-thread element offsets of the direct-to-LDS loads (the same for every tile).
-    int goff[NI];
+    // (byte offsets from the tile's first element)
+    uint32_t goff[NI];
 #pragma unroll
-    for (int u = 0; u < NI; ++u) goff[u] = TL::load_src(u, w, lane);
+    for (int u = 0; u < NI; ++u) goff[u] = 2u * (uint32_t)TL::load_src(u, w, lane);
     // LDS byte offsets of this lane's K reads (A operand of S^T) and V transposing reads.
     int koff[D / 16];
 #pragma unroll
@@ -116,8 +117,8 @@ __global__ __launch_bounds__(256) void fwd_bf16_t64_kernel(const FwdArgs a)
         const unsigned short* Vt = V + (int64_t)kb * T * D;
 #pragma unroll
         for (int u = 0; u < NI; ++u) {
-            __builtin_amdgcn_global_load_lds((glb_void*)(Kt + goff[u]), (lds_void*)(kd + TL::load_dst(u, w)), 16, 0, 0);
-            __builtin_amdgcn_global_load_lds((glb_void*)(Vt + goff[u]), (lds_void*)(vd + TL::load_dst(u, w)), 16, 0, 0);
+            __builtin_amdgcn_global_load_lds((glb_void*)sgpr_base_plus(Kt, goff[u]), (lds_void*)(kd + TL::load_dst(u, w)), 16, 0, 0);
+            __builtin_amdgcn_global_load_lds((glb_void*)sgpr_base_plus(Vt, goff[u]), (lds_void*)(vd + TL::load_dst(u, w)), 16, 0, 0);
         }
     };
 

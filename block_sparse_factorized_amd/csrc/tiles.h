@@ -78,6 +78,18 @@ __device__ static inline void wait_vmcnt()
     __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
+// Global address of byte offset off from a wave-uniform base, in the form
+// the loads encode as base (SGPRs) + 32-bit offset (VGPR).  The empty asm
+// keeps the compiler from hoisting the offset's 64-bit extension out of the
+// loop, which would turn every load's address into a 64-bit vector add.
+__device__ static inline const void* sgpr_base_plus(const void* base, uint32_t off)
+{
+#if defined(__HIP_DEVICE_COMPILE__)  // the constraint names a GPU register class
+    asm volatile("" : "+v"(off));
+#endif
+    return (const unsigned char*)base + off;
+}
+
 // Two transposing 8-byte LDS reads (ds_read_b64_tr_b16) forming one 8 x bf16 operand.
 __device__ static inline bf16x8 lds_read_tr8(const unsigned char* p0, const unsigned char* p1)
 {
