@@ -165,12 +165,22 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(const BwdArgs a)
         }
     };
 
+    int4 st_cur = {0, 0, 0, 0}, st_nxt = {0, 0, 0, 0};
+    if (nblk > 0) {
+        st_cur = ld_uniform(&L.kgrp_step[p0]);
+        st_nxt = ld_uniform(&L.kgrp_step[p0 + min(1, nblk - 1)]);
+    }
+
     // One step: start the next tile's loads into (qn, on, rn), accumulate the
     // tile in (qc, oc, rc), then wait for the next tile.
     auto step_tile = [&](int t, const unsigned char* qc, const unsigned char* oc, const float* rc,
                          unsigned char* qn, unsigned char* on, float* rn) {
-        if (t + 1 < nblk) issue(ld_uniform(&L.kgrp_step[p0 + t + 1]).x, qn, on, rn);
-        const int4 step = ld_uniform(&L.kgrp_step[p0 + t]);
+        // Step records are loaded two steps ahead, so no list read is waited
+        // for in the step that uses it.
+        const int4 step = st_cur;
+        if (t + 1 < nblk) issue(st_nxt.x, qn, on, rn);
+        st_cur = st_nxt;
+        st_nxt = ld_uniform(&L.kgrp_step[p0 + min(t + 2, nblk - 1)]);
         const int mid = member ? step.z : step.y;  // -2: this key block is not listed
         if (kb >= 0 && mid != -2) {
             // Transposed lane-mask planes (set 0 for a full block, unused),
@@ -248,7 +258,7 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(const BwdArgs a)
         __syncthreads();
     };
 
-    if (nblk > 0) issue(ld_uniform(&L.kgrp_step[p0]).x, qbuf0, obuf0, rbuf0);
+    if (nblk > 0) issue(st_cur.x, qbuf0, obuf0, rbuf0);
     wait_vmem();
     __syncthreads();
     for (int t = 0; t < nblk; t += 2) {
@@ -355,12 +365,22 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D == 64 ? 4
         }
     };
 
+    int4 st_cur = {0, 0, 0, 0}, st_nxt = {0, 0, 0, 0};
+    if (nblk > 0) {
+        st_cur = ld_uniform(&L.qgrp_step[p0]);
+        st_nxt = ld_uniform(&L.qgrp_step[p0 + min(1, nblk - 1)]);
+    }
+
     // One step: start the next tile's loads into (kn, vn), accumulate the
     // tile in (kc, vc), then wait for the next tile.
     auto step_tile = [&](int t, const unsigned char* kc, const unsigned char* vc, unsigned char* kn,
                          unsigned char* vn) {
-        if (t + 1 < nblk) issue(ld_uniform(&L.qgrp_step[p0 + t + 1]).x, kn, vn);
-        const int4 step = ld_uniform(&L.qgrp_step[p0 + t]);
+        // Step records are loaded two steps ahead, so no list read is waited
+        // for in the step that uses it.
+        const int4 step = st_cur;
+        if (t + 1 < nblk) issue(st_nxt.x, kn, vn);
+        st_cur = st_nxt;
+        st_nxt = ld_uniform(&L.qgrp_step[p0 + min(t + 2, nblk - 1)]);
         const int mid = member ? step.z : step.y;  // -2: not in this block's list
         if (qb >= 0 && mid != -2) {
             // Lane-mask planes (set 0 for a full block, unused) first, so the
@@ -427,7 +447,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D == 64 ? 4
         __syncthreads();
     };
 
-    if (nblk > 0) issue(ld_uniform(&L.qgrp_step[p0]).x, kbuf0, vbuf0);
+    if (nblk > 0) issue(st_cur.x, kbuf0, vbuf0);
     wait_vmem();
     __syncthreads();
     for (int t = 0; t < nblk; t += 2) {

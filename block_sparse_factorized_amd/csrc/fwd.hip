@@ -122,12 +122,22 @@ __global__ __launch_bounds__(256) void fwd_bf16_t64_kernel(const FwdArgs a)
         }
     };
 
+    int4 st_cur = {0, 0, 0, 0}, st_nxt = {0, 0, 0, 0};
+    if (nblk > 0) {
+        st_cur = ld_uniform(&L.qgrp_step[p0]);
+        st_nxt = ld_uniform(&L.qgrp_step[p0 + min(1, nblk - 1)]);
+    }
+
     // One step: start the loads of tile t + 1 into (kn, vn), fold the tile
     // in (kc, vc) into the online softmax, then wait for tile t + 1.
     auto step_tile = [&](int t, const unsigned char* kc, const unsigned char* vc, unsigned char* kn,
                          unsigned char* vn) {
-        if (t + 1 < nblk) issue(ld_uniform(&L.qgrp_step[p0 + t + 1]).x, kn, vn);
-        const int4 step = ld_uniform(&L.qgrp_step[p0 + t]);
+        // Step records are loaded two steps ahead, so no list read is waited
+        // for in the step that uses it.
+        const int4 step = st_cur;
+        if (t + 1 < nblk) issue(st_nxt.x, kn, vn);
+        st_cur = st_nxt;
+        st_nxt = ld_uniform(&L.qgrp_step[p0 + min(t + 2, nblk - 1)]);
         const int mid = member ? step.z : step.y;  // -2: not in this block's list
         if (qb >= 0 && mid != -2) {
             // Lane masks of every score register, one 64-bit plane each, loaded
@@ -231,7 +241,7 @@ __global__ __launch_bounds__(256) void fwd_bf16_t64_kernel(const FwdArgs a)
         __syncthreads();  // ... for every wave, and every wave is done with tile t
     };
 
-    if (nblk > 0) issue(ld_uniform(&L.qgrp_step[p0]).x, kbuf0, vbuf0);
+    if (nblk > 0) issue(st_cur.x, kbuf0, vbuf0);
     wait_vmem();
     __syncthreads();
     for (int t = 0; t < nblk; t += 2) {
