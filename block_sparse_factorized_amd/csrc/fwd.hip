@@ -109,7 +109,10 @@ __global__ __launch_bounds__(256) void fwd_bf16_t64_kernel(const FwdArgs a)
     for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
         for (int i = 0; i < 16; ++i) oacc[dt][i] = 0.f;
-    float m_ref = -INFINITY, l_run = 0.f;
+    // Running reference max m_ref, mc = m_ref * c2 (0 while m_ref = -inf),
+    // running sum l_run; no_ref: some row of the wave has no reference yet.
+    float m_ref = -INFINITY, mc = 0.f, l_run = 0.f;
+    bool no_ref = true;
     const float c2 = a.scale_log2;
 
     auto issue = [&](int kb, unsigned char* kd, unsigned char* vd) {
@@ -140,78 +143,109 @@ __global__ __launch_bounds__(256) void fwd_bf16_t64_kernel(const FwdArgs a)
         st_nxt = ld_uniform(&L.qgrp_step[p0 + min(t + 2, nblk - 1)]);
         const int mid = member ? step.z : step.y;  // -2: not in this block's list
         if (qb >= 0 && mid != -2) {
-            // Lane masks of every score register, one 64-bit plane each, loaded
-            // into SGPRs before the products so the loads overlap them (a full
-            // block reads plane set 0, unused).  The constant address space lets
-            // these wave-uniform loads be scalar loads.
+            // Lane masks of every score register, one 64-bit plane each (a full
+            // block reads plane set 0, unused); the constant address space makes
+            // these wave-uniform loads scalar loads.
             const_u64* pl = (const_u64*)(L.planes + ((int64_t)(mid >= 0 ? mid : 0) * 2 + wr) * 32);
-            uint64_t pln[32];
-#pragma unroll
-            for (int r = 0; r < 32; ++r) pln[r] = pl[r];
             // A 32-key half with no allowed element in this wave's rows (quadrant
             // (query half wr, key half kt) of the mask empty) has only zero
             // weights: its scores, softmax and products are skipped, since they
-            // would only add zeros to the output.
-            const unsigned quad = (unsigned)step.w >> (4 * member);
-            bool live[2];
-#pragma unroll
-            for (int kt = 0; kt < 2; ++kt) live[kt] = (quad >> (2 * wr + kt)) & 1u;
+            // would only add zeros to the output.  Bit kt of lv: half kt is live.
+            const unsigned lv = ((unsigned)step.w >> (4 * member + 2 * wr)) & 3u;
 
             // S^T = K Q^T: register i of s[kt] holds key 32*kt + 8*(i/4) + 4*hh + i%4 of query n.
-            // A live half's operand reads first, then its products.
+            // A live half's operand reads first, then its products; then the
+            // disallowed elements of a partial block to -inf.
             f32x16 s[2];
-#pragma unroll
-            for (int kt = 0; kt < 2; ++kt)
-                if (live[kt]) {
-                    bf16x8 kop[D / 16];
-#pragma unroll
-                    for (int c = 0; c < D / 16; ++c) kop[c] = *(const bf16x8*)(kc + koff[c] + kt * 32 * TL::kRow);
-#pragma unroll
-                    for (int i = 0; i < 16; ++i) s[kt][i] = 0.f;
-#pragma unroll
-                    for (int c = 0; c < D / 16; ++c)
-                        s[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop[c], qop[c], s[kt], 0, 0, 0);
-                }
-
-            // Partial block: disallowed elements to -inf.
-            if (mid >= 0) {
+            auto scores = [&]() {
 #pragma unroll
                 for (int kt = 0; kt < 2; ++kt)
-                    if (live[kt]) {
+                    if ((lv >> kt) & 1u) {
+                        // this half's 16 planes into SGPRs first, so the loads
+                        // overlap the products
+                        uint64_t pln[16];
+                        if (mid >= 0) {
 #pragma unroll
-                        for (int i = 0; i < 16; ++i)
-                            s[kt][i] = __builtin_amdgcn_inverse_ballot_w64(pln[16 * kt + i]) ? s[kt][i] : -INFINITY;
+                            for (int r = 0; r < 16; ++r) pln[r] = pl[16 * kt + r];
+                        }
+                        bf16x8 kop[D / 16];
+#pragma unroll
+                        for (int c = 0; c < D / 16; ++c) kop[c] = *(const bf16x8*)(kc + koff[c] + kt * 32 * TL::kRow);
+#pragma unroll
+                        for (int i = 0; i < 16; ++i) s[kt][i] = 0.f;
+#pragma unroll
+                        for (int c = 0; c < D / 16; ++c)
+                            s[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop[c], qop[c], s[kt], 0, 0, 0);
+                        if (mid >= 0) {
+#pragma unroll
+                            for (int i = 0; i < 16; ++i)
+                                s[kt][i] = __builtin_amdgcn_inverse_ballot_w64(pln[i]) ? s[kt][i] : -INFINITY;
+                        }
                     }
-            }
-            float mx = -INFINITY;
+            };
+            // Weights p = exp2(c2 s - mc) of the live halves, in place; returns
+            // this lane's sum of them.
+            auto weights = [&]() {
+                float lsum = 0.f;
 #pragma unroll
-            for (int kt = 0; kt < 2; ++kt)
-                if (live[kt]) {
+                for (int kt = 0; kt < 2; ++kt)
+                    if ((lv >> kt) & 1u) {
 #pragma unroll
-                    for (int i = 0; i < 16; ++i) mx = __builtin_fmaxf(mx, s[kt][i]);
-                }
-            mx = half_max(mx);
+                        for (int i = 0; i < 16; ++i) {
+                            const float p = __builtin_amdgcn_exp2f(fmaf(s[kt][i], c2, -mc));
+                            s[kt][i] = p;
+                            lsum += p;
+                        }
+                    }
+                return lsum;
+            };
+            scores();
 
-            // Lazy rescale: keep the reference max unless some row's max grew by
-            // more than 2^8 in the exponent (then every lane of the wave rescales).
-            const float m_new = __builtin_fmaxf(m_ref, mx);
-            if (__builtin_amdgcn_ballot_w64((m_new - m_ref) * c2 > 8.f)) {
-                const float alpha = m_new == -INFINITY ? 1.f : __builtin_amdgcn_exp2f((m_ref - m_new) * c2);
-                l_run *= alpha;
-#pragma unroll
-                for (int dt = 0; dt < D / 32; ++dt)
-#pragma unroll
-                    for (int i = 0; i < 16; ++i) oacc[dt][i] *= alpha;
-                m_ref = m_new;
+            // Lazy reference max.  Once every row of the wave has a reference,
+            // the tile's max is not computed: the weights are taken against the
+            // reference directly, and a per-lane sum of at most 2^8 shows that
+            // no weight exceeds 2^8 (the bound the reference is kept to).  Else
+            // (no reference yet, or a larger sum: some row's max moved up) the
+            // scores are formed again and the exact path below moves the
+            // reference to the row max, rescaling the accumulator.
+            bool exact = no_ref;
+            if (!exact) {
+                const float lsum = weights();
+                exact = __builtin_amdgcn_ballot_w64(!(lsum <= 256.f)) != 0;  // also catches inf
+                if (exact)
+                    scores();
+                else
+                    l_run += lsum;
             }
-            const float mc = m_ref == -INFINITY ? 0.f : m_ref * c2;
+            if (exact) {
+                float mx = -INFINITY;
+#pragma unroll
+                for (int kt = 0; kt < 2; ++kt)
+                    if ((lv >> kt) & 1u) {
+#pragma unroll
+                        for (int i = 0; i < 16; ++i) mx = __builtin_fmaxf(mx, s[kt][i]);
+                    }
+                mx = half_max(mx);
+                const float m_new = __builtin_fmaxf(m_ref, mx);
+                if (__builtin_amdgcn_ballot_w64(m_new > m_ref)) {
+                    const float alpha = m_new == -INFINITY ? 1.f : __builtin_amdgcn_exp2f((m_ref - m_new) * c2);
+                    l_run *= alpha;
+#pragma unroll
+                    for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+                        for (int i = 0; i < 16; ++i) oacc[dt][i] *= alpha;
+                    m_ref = m_new;
+                    mc = m_ref == -INFINITY ? 0.f : m_ref * c2;
+                }
+                no_ref = __builtin_amdgcn_ballot_w64(m_ref == -INFINITY) != 0;
+                l_run += weights();
+            }
 
             // P^T (chunk cc of P^T is registers 8*(cc%2)..+7 of s[cc/2]), then
-            // O^T += V^T P^T, one 32-key half at a time; the half's V^T operands
-            // are read before its exponentials so the LDS latency overlaps them.
+            // O^T += V^T P^T, one live 32-key half at a time.
 #pragma unroll
             for (int kt = 0; kt < 2; ++kt)
-                if (live[kt]) {
+                if ((lv >> kt) & 1u) {
                     bf16x8 vop[2][D / 32];
 #pragma unroll
                     for (int h = 0; h < 2; ++h)
@@ -221,14 +255,6 @@ __global__ __launch_bounds__(256) void fwd_bf16_t64_kernel(const FwdArgs a)
                             vop[h][dt] = lds_read_tr8(vc + voff[0][dt] + cc * 16 * TL::kRow,
                                                       vc + voff[1][dt] + cc * 16 * TL::kRow);
                         }
-                    float lsum = 0.f;
-#pragma unroll
-                    for (int i = 0; i < 16; ++i) {
-                        const float p = __builtin_amdgcn_exp2f(fmaf(s[kt][i], c2, -mc));
-                        s[kt][i] = p;
-                        lsum += p;
-                    }
-                    l_run += lsum;
                     const bf16x8 pb[2] = {pack8(s[kt], 0), pack8(s[kt], 8)};
 #pragma unroll
                     for (int h = 0; h < 2; ++h)
