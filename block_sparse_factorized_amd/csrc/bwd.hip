@@ -50,7 +50,7 @@ __device__ inline void zero(f32x16& x)
 }
 
 // ---------------------------------------------------------------------------
-// Row terms, D/8 threads per row:  D_i = sum_t dO_it O_it  and
+// Row terms, D/8 threads per row:  -D_i = -sum_t dO_it O_it  and
 // nl2_i = -lse_i * log2(e)  (-inf for an empty row, whose P is all zero).
 template <int D>
 __global__ __launch_bounds__(256) void bwd_rowterms_kernel(const BwdArgs a, int64_t rows)
@@ -69,7 +69,7 @@ __global__ __launch_bounds__(256) void bwd_rowterms_kernel(const BwdArgs a, int6
 #pragma unroll
     for (int off = 1; off < TPR; off <<= 1) acc += __shfl_xor(acc, off);
     if (row < rows && part == 0) {
-        a.delta[row] = acc;
+        a.ndelta[row] = -acc;
         const float l = a.lse[row];
         a.nl2[row] = l == -INFINITY ? -INFINITY : -l * kLog2e;
     }
@@ -98,7 +98,7 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(const BwdArgs a)
     __shared__ __attribute__((aligned(1024))) unsigned char obuf0[TL::kBytes];
     __shared__ __attribute__((aligned(1024))) unsigned char qbuf1[TL::kBytes];
     __shared__ __attribute__((aligned(1024))) unsigned char obuf1[TL::kBytes];
-    __shared__ __attribute__((aligned(16))) float rbuf0[2 * T];  // nl2[64], then D[64]
+    __shared__ __attribute__((aligned(16))) float rbuf0[2 * T];  // nl2[64], then -D[64]
     __shared__ __attribute__((aligned(16))) float rbuf1[2 * T];
 
     const int tid = threadIdx.x, lane = tid & 63;
@@ -114,7 +114,7 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(const BwdArgs a)
     const unsigned short* Q = (const unsigned short*)a.q + head;
     const unsigned short* dO = (const unsigned short*)a.dout + head;
     const float* nl2g = a.nl2 + (int64_t)bh * a.n;
-    const float* dlg = a.delta + (int64_t)bh * a.n;
+    const float* dlg = a.ndelta + (int64_t)bh * a.n;
     const int k_local = 32 * wr + n32;
     const int64_t k_row = (int64_t)(kb < 0 ? 0 : kb) * T + k_local;
 
@@ -159,7 +159,7 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(const BwdArgs a)
             __builtin_amdgcn_global_load_lds((glb_void*)sgpr_base_plus(Qt, goff[u]), (lds_void*)(qd + TL::load_dst(u, w)), 16, 0, 0);
             __builtin_amdgcn_global_load_lds((glb_void*)sgpr_base_plus(Ot, goff[u]), (lds_void*)(od + TL::load_dst(u, w)), 16, 0, 0);
         }
-        if (w < 2) {  // wave 0: nl2, wave 1: D
+        if (w < 2) {  // wave 0: nl2, wave 1: -D
             const float* src = (w == 0 ? nl2g : dlg) + (int64_t)qb * T + lane;
             __builtin_amdgcn_global_load_lds((glb_void*)src, (lds_void*)(rd + T * w), 4, 0, 0);
         }
@@ -210,8 +210,14 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(const BwdArgs a)
                         qa[c] = *(const bf16x8*)(qc + aoff[c] + qt * 32 * TL::kRow);
                         oa[c] = *(const bf16x8*)(oc + aoff[c] + qt * 32 * TL::kRow);
                     }
+                    // dP starts from -D of its query rows, so the product gives dP - D.
                     zero(s);
-                    zero(dp);
+#pragma unroll
+                    for (int g = 0; g < 4; ++g) {
+                        const f32x4 nd = *(const f32x4*)&rc[T + 32 * qt + 8 * g + 4 * hh];
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) dp[4 * g + e] = nd[e];
+                    }
 #pragma unroll
                     for (int c = 0; c < D / 16; ++c) {
                         s = mfma(qa[c], kop[c], s);
@@ -234,13 +240,12 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(const BwdArgs a)
 #pragma unroll
                     for (int g = 0; g < 4; ++g) {
                         const f32x4 nl = *(const f32x4*)&rc[32 * qt + 8 * g + 4 * hh];
-                        const f32x4 dd = *(const f32x4*)&rc[T + 32 * qt + 8 * g + 4 * hh];
 #pragma unroll
                         for (int e = 0; e < 4; ++e) {
                             const int i = 4 * g + e;
                             const float p = __builtin_amdgcn_exp2f(fmaf(s[i], c2, nl[e]));
                             s[i] = p;
-                            dp[i] = p * (dp[i] - dd[e]);
+                            dp[i] = p * dp[i];
                         }
                     }
                     const bf16x8 pb[2] = {pack8(s, 0), pack8(s, 8)};
@@ -334,7 +339,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D == 64 ? 4
         }
     }
     const float nl2 = a.nl2[(int64_t)bh * a.n + q_row];
-    const float d_i = a.delta[(int64_t)bh * a.n + q_row];
+    const float nd_i = a.ndelta[(int64_t)bh * a.n + q_row];
     // (byte offsets from the tile's first element)
     uint32_t goff[NI];
 #pragma unroll
@@ -434,7 +439,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D == 64 ? 4
 #pragma unroll
                     for (int i = 0; i < 16; ++i) {
                         const float p = __builtin_amdgcn_exp2f(fmaf(s[i], c2, nl2));
-                        dp[i] = p * (dp[i] - d_i);
+                        dp[i] = p * (dp[i] + nd_i);
                     }
                     const bf16x8 db[2] = {pack8(dp, 0), pack8(dp, 8)};
 #pragma unroll

@@ -457,7 +457,7 @@ int bwd_call(const char* fn, int stages, const sa_layout_t* const* head_layout, 
     a.dq = dq;
     a.dk = dk;
     a.dv = dv;
-    a.delta = (float*)workspace;
+    a.ndelta = (float*)workspace;
     a.nl2 = (float*)workspace + (size_t)B * H * n;
     a.n = n;
     a.H = H;

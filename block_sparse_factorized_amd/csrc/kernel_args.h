@@ -47,7 +47,7 @@ struct BwdArgs {
     void* dq;
     void* dk;
     void* dv;
-    float* delta;  // workspace: D_i = sum_t dO_it * O_it, fp32 [B*H*n]
+    float* ndelta;  // workspace: -D_i = -sum_t dO_it * O_it, fp32 [B*H*n]
     float* nl2;    // workspace: -lse_i * log2(e) (-inf for an empty row), fp32 [B*H*n]
     int64_t n;
     int32_t H;

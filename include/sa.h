@@ -149,8 +149,8 @@ int sa_fwd(const sa_layout_t* const* head_layout, int32_t B, int32_t H, int64_t 
            int dtype, float scale, const void* q, const void* k, const void* v, void* o,
            float* lse, void* stream);
 
-/* Bytes of device workspace sa_bwd needs: two fp32 row terms per row, D_i
- * = sum_t dO_it O_it and -lse_i * log2(e). */
+/* Bytes of device workspace sa_bwd needs: two fp32 row terms per row,
+ * -D_i = -sum_t dO_it O_it and -lse_i * log2(e). */
 size_t sa_bwd_workspace_size(int32_t B, int32_t H, int64_t n, int32_t d);
 
 /*
@@ -172,7 +172,7 @@ int sa_bwd(const sa_layout_t* const* head_layout, int32_t B, int32_t H, int64_t 
  * them themselves (for instance dQ and dK/dV on two streams once the row
  * terms are ready).  Arguments mean what they mean for sa_bwd; each call
  * reads and writes only the pointers it takes.
- *   sa_bwd_rowterms  the row terms D_i = sum_t dO_it O_it and -lse_i log2(e)
+ *   sa_bwd_rowterms  the row terms -D_i = -sum_t dO_it O_it and -lse_i log2(e)
  *                    into the workspace
  *   sa_bwd_dkdv      dK, dV (reads the row terms from the workspace), one
  *                    workgroup per pair of key blocks walking their query
