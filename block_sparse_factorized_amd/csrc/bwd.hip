@@ -110,12 +110,21 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(const BwdArgs a)
     const DevLayout L = a.heads.lay[a.heads.head_lay[bh % a.H]];
     const int2 pair = ld_uniform(&L.kgrp_blk[grp]);
     const int kb = member ? pair.y : pair.x;  // -1: this wave has no keys
+    // Key half this wave holds and the query halves it takes: normally its
+    // own half (wr) against both query halves; when the member's whole list
+    // only has allowed elements in one key half, both waves hold that half
+    // and wave wr takes query half wr (their partial dK, dV are summed at
+    // the end), so neither wave idles.
+    const int modes = ld_uniform(&L.kgrp_mode[grp]);
+    const int kmode = (modes >> (2 * member)) & 3;
+    const int kh = kmode ? kmode - 1 : wr;
+    const unsigned qsel = kmode ? 1u << wr : 3u;
     const int64_t head = (int64_t)bh * a.n * D;
     const unsigned short* Q = (const unsigned short*)a.q + head;
     const unsigned short* dO = (const unsigned short*)a.dout + head;
     const float* nl2g = a.nl2 + (int64_t)bh * a.n;
     const float* dlg = a.ndelta + (int64_t)bh * a.n;
-    const int k_local = 32 * wr + n32;
+    const int k_local = 32 * kh + n32;
     const int64_t k_row = (int64_t)(kb < 0 ? 0 : kb) * T + k_local;
 
     bf16x8 kop[D / 16], vop[D / 16];
@@ -187,14 +196,14 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(const BwdArgs a)
             // loaded before the products so the scalar loads overlap them.
             // A 32-query half is live when the mask has an allowed element in
             // quadrant (query half qt, key half wr).
-            const_u64* pl = (const_u64*)(L.planes_t + ((int64_t)(mid >= 0 ? mid : 0) * 2 + wr) * 32);
+            const_u64* pl = (const_u64*)(L.planes_t + ((int64_t)(mid >= 0 ? mid : 0) * 2 + kh) * 32);
             uint64_t pln[32];
 #pragma unroll
             for (int r = 0; r < 32; ++r) pln[r] = pl[r];
             const unsigned quad = (unsigned)step.w >> (4 * member);
             bool live[2];
 #pragma unroll
-            for (int qt = 0; qt < 2; ++qt) live[qt] = (quad >> (2 * qt + wr)) & 1u;
+            for (int qt = 0; qt < 2; ++qt) live[qt] = ((quad >> (2 * qt + kh)) & (qsel >> qt) & 1u) != 0;
 
             // One 32-query half at a time; a half with no allowed element for
             // this wave's keys is skipped entirely (it would only add zeros).
@@ -271,10 +280,47 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(const BwdArgs a)
         if (t + 1 < nblk) step_tile(t + 1, qbuf1, obuf1, rbuf1, qbuf0, obuf0, rbuf0);
     }
 
+    // Shared-half members: wave 1 hands its partial sums to wave 0 through
+    // the (now idle) tile buffers, laid out [dt][i][lane].
+    if (modes != 0) {
+        float* rk = (float*)(member ? qbuf1 : qbuf0);
+        float* rv = (float*)(member ? obuf1 : obuf0);
+        if (kmode && wr == 1) {
+#pragma unroll
+            for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+                for (int i = 0; i < 16; ++i) {
+                    rk[(dt * 16 + i) * 64 + lane] = dk[dt][i];
+                    rv[(dt * 16 + i) * 64 + lane] = dv[dt][i];
+                }
+        }
+        __syncthreads();
+        if (kmode && wr == 0) {
+#pragma unroll
+            for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+                for (int i = 0; i < 16; ++i) {
+                    dk[dt][i] += rk[(dt * 16 + i) * 64 + lane];
+                    dv[dt][i] += rv[(dt * 16 + i) * 64 + lane];
+                }
+        }
+    }
     if (kb < 0) return;
-    // Register i of dk[dt]/dv[dt]: d = 32*dt + 8*(i/4) + 4*hh + i%4 of key k_row.
-    unsigned short* DK = (unsigned short*)a.dk + head + k_row * D;
-    unsigned short* DV = (unsigned short*)a.dv + head + k_row * D;
+    // Each wave writes one 32-key half of its block.  In a shared-half member
+    // wave 0 writes the shared half, wave 1 the other half, whose keys no
+    // query reaches: zeros.
+    int64_t out_row = k_row;
+    if (kmode && wr == 1) {
+        out_row = (int64_t)kb * T + 32 * (1 - kh) + n32;
+#pragma unroll
+        for (int dt = 0; dt < D / 32; ++dt) {
+            zero(dk[dt]);
+            zero(dv[dt]);
+        }
+    }
+    // Register i of dk[dt]/dv[dt]: d = 32*dt + 8*(i/4) + 4*hh + i%4 of key out_row.
+    unsigned short* DK = (unsigned short*)a.dk + head + out_row * D;
+    unsigned short* DV = (unsigned short*)a.dv + head + out_row * D;
 #pragma unroll
     for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll

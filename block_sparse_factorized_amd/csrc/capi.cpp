@@ -72,6 +72,10 @@ int device_layout(sa_layout* L, int dev, DevLayout* out)
         off_gstep[k] = al(off_gblk[k] + gs[k]->blk.size() * 4);
         cur = al(off_gstep[k] + gs[k]->step.size() * 4);
     }
+    // Per key-block pair: which key halves each member's list ever touches.
+    const size_t n_kgroups = L->kgroups.ptr.empty() ? 0 : L->kgroups.ptr.size() - 1;
+    const size_t off_kmode = cur;
+    cur = al(off_kmode + n_kgroups * 4);
     size_t total = cur;
     std::vector<unsigned char> host(total, 0);
     if (nwords) {
@@ -144,6 +148,25 @@ int device_layout(sa_layout* L, int dev, DevLayout* out)
             st[x + 3] = (int32_t)(quad_of(st[x + 1]) | quad_of(st[x + 2]) << 4);
         }
     }
+    // Key-block pairs: a member whose list only ever has allowed elements in
+    // one 32-key half gets mode 1 + that half (its two waves then share the
+    // half and split the query halves), else mode 0.  Bits 0-1: member a,
+    // bits 2-3: member b.
+    {
+        const int32_t* st = (const int32_t*)&host[off_gstep[1]];
+        int32_t* km = (int32_t*)&host[off_kmode];
+        for (size_t g = 0; g < n_kgroups; ++g) {
+            uint32_t seen = 0;
+            for (int32_t x = L->kgroups.ptr[g]; x < L->kgroups.ptr[g + 1]; ++x) seen |= (uint32_t)st[4 * x + 3];
+            int32_t mode = 0;
+            for (int m = 0; m < 2; ++m) {
+                const uint32_t q = (seen >> (4 * m)) & 0xFu;
+                const bool h0 = (q & 0x5u) != 0, h1 = (q & 0xAu) != 0;  // key half 0: bits 0, 2
+                if (h0 != h1) mode |= (h0 ? 1 : 2) << (2 * m);
+            }
+            km[g] = mode;
+        }
+    }
     void* mem = nullptr;
     hipError_t e = hipMalloc(&mem, total);
     if (e != hipSuccess) return fail(SA_ERR_ALLOC, "layout upload: hipMalloc(%zu): %s", total, hipGetErrorString(e));
@@ -170,6 +193,7 @@ int device_layout(sa_layout* L, int dev, DevLayout* out)
     v.kgrp_ptr = (const int32_t*)(b + off_gptr[1]);
     v.kgrp_blk = (const int2*)(b + off_gblk[1]);
     v.kgrp_step = (const int4*)(b + off_gstep[1]);
+    v.kgrp_mode = (const int32_t*)(b + off_kmode);
     L->dev_mem[dev] = mem;
     L->dev[dev] = v;
     *out = v;

@@ -50,6 +50,10 @@ struct DevLayout {
     const int32_t* kgrp_ptr;
     const int2* kgrp_blk;
     const int4* kgrp_step;
+    // Per key-block pair, 2 bits per member (a: bits 0-1, b: bits 2-3): 0, or
+    // 1 + h when the member's whole query list has allowed elements only in
+    // its 32-key half h.
+    const int32_t* kgrp_mode;
 };
 
 // Host-side pairing of one listing (see DevLayout).

@@ -201,6 +201,35 @@ def test_deterministic_bitwise_repeat():
         assert torch.equal(r1[t], r2[t]), t
 
 
+@pytest.mark.parametrize("pats,n,d", [
+    ([("fixed_a", 128, 32), ("fixed_b", 128, 32)], 512, 64),
+    ([("fixed_b", 64, 16), ("strided_b", 100, 1)], 256, 64),
+    ([("strided_a", 37, 1), ("fixed_b", 96, 17)], 448, 128),
+    ([("fixed_b", 256, 8), ("strided_b", 128, 1)], 512, 64),
+])
+def test_every_output_element_written(pats, n, d):
+    """Outputs pre-filled with NaN come back identical to a normal run: every
+    element of O, lse, dQ, dK and dV is written (keys no query reaches get
+    exact zeros), whatever the pattern leaves empty."""
+    H = len(pats)
+    x = workloads.custom_inputs((2, H, n, d), torch.bfloat16, seed=n + d)
+    lays = layouts_for(pats, n, 64)
+    q, k, v, do = (x[t].to(DEV) for t in ("q", "k", "v", "do"))
+    ref_o, ref_lse = sa.sa_fwd(q, k, v, lays, 1.0)
+    ref = sa.sa_bwd(q, k, v, ref_o, ref_lse, do, lays, 1.0)
+    nan = float("nan")
+    o = torch.full_like(q, nan)
+    lse = torch.full(q.shape[:3], nan, dtype=torch.float32, device=DEV)
+    sa.sa_fwd(q, k, v, lays, 1.0, o=o, lse=lse)
+    dq, dk, dv = (torch.full_like(q, nan) for _ in range(3))
+    sa.sa_bwd(q, k, v, o, lse, do, lays, 1.0, dq=dq, dk=dk, dv=dv)
+    torch.cuda.synchronize()
+    assert torch.equal(o, ref_o) and torch.equal(lse, ref_lse)
+    for got, want, nm in zip((dq, dk, dv), ref, ("dq", "dk", "dv")):
+        assert not torch.isnan(got.float()).any(), nm
+        assert torch.equal(got, want), nm
+
+
 def test_noncurrent_stream():
     """Kernels run on the stream they are given."""
     n = 512
