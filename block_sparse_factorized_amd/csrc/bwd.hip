@@ -192,11 +192,11 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(const BwdArgs a)
         st_nxt = ld_uniform(&L.kgrp_step[p0 + min(t + 2, nblk - 1)]);
         const int mid = member ? step.z : step.y;  // -2: this key block is not listed
         if (kb >= 0 && mid != -2) {
-            // Transposed lane-mask planes (set 0 for a full block, unused),
+            // Transposed lane-mask planes (set 0, all ones, for a full block),
             // loaded before the products so the scalar loads overlap them.
             // A 32-query half is live when the mask has an allowed element in
             // quadrant (query half qt, key half wr).
-            const_u64* pl = (const_u64*)(L.planes_t + ((int64_t)(mid >= 0 ? mid : 0) * 2 + kh) * 32);
+            const_u64* pl = (const_u64*)(L.planes_t + ((int64_t)(mid + 1) * 2 + kh) * 32);
             uint64_t pln[32];
 #pragma unroll
             for (int r = 0; r < 32; ++r) pln[r] = pl[r];
@@ -434,11 +434,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D == 64 ? 4
         st_nxt = ld_uniform(&L.qgrp_step[p0 + min(t + 2, nblk - 1)]);
         const int mid = member ? step.z : step.y;  // -2: not in this block's list
         if (qb >= 0 && mid != -2) {
-            // Lane-mask planes (set 0 for a full block, unused) first, so the
+            // Lane-mask planes (set 0, all ones, for a full block) first, so the
             // scalar loads overlap the products.  A 32-key half is live when
             // the mask has an allowed element in quadrant (query half wr, key
             // half kt).
-            const_u64* pl = (const_u64*)(L.planes + ((int64_t)(mid >= 0 ? mid : 0) * 2 + wr) * 32);
+            const_u64* pl = (const_u64*)(L.planes + ((int64_t)(mid + 1) * 2 + wr) * 32);
             uint64_t pln[32];
 #pragma unroll
             for (int r = 0; r < 32; ++r) pln[r] = pl[r];

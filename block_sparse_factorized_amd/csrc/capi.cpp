@@ -53,8 +53,8 @@ int device_layout(sa_layout* L, int dev, DevLayout* out)
     auto al = [](size_t x) { return (x + 255) & ~(size_t)255; };
     size_t off_masks = 0;
     size_t off_masks_t = al(off_masks + nwords * 8);
-    // At least one plane set, so kernels may always load set 0.
-    const size_t nplanes = L->T == 64 ? (size_t)std::max<int64_t>(L->n_masks, 1) * 64 : 0;
+    // Plane set 0 is all ones (a full block); mask m is set m + 1.
+    const size_t nplanes = L->T == 64 ? (size_t)(L->n_masks + 1) * 64 : 0;
     size_t off_planes = al(off_masks_t + nwords * 8);
     size_t off_planes_t = al(off_planes + nplanes * 8);
     size_t off_row_ptr = al(off_planes_t + nplanes * 8);
@@ -113,8 +113,8 @@ int device_layout(sa_layout* L, int dev, DevLayout* out)
                         a |= bit(m, outer, inner) << lane;
                         b |= bit(m, inner, outer) << lane;
                     }
-                    pl[(m * 2 + w) * 32 + reg] = a;
-                    pt[(m * 2 + w) * 32 + reg] = b;
+                    pl[((m + 1) * 2 + w) * 32 + reg] = a;
+                    pt[((m + 1) * 2 + w) * 32 + reg] = b;
                 }
     }
     memcpy(&host[off_row_ptr], L->row_ptr.data(), nqb1 * 4);

@@ -144,9 +144,9 @@ __global__ __launch_bounds__(256) void fwd_bf16_t64_kernel(const FwdArgs a)
         const int mid = member ? step.z : step.y;  // -2: not in this block's list
         if (qb >= 0 && mid != -2) {
             // Lane masks of every score register, one 64-bit plane each (a full
-            // block reads plane set 0, unused); the constant address space makes
+            // block reads plane set 0, all ones); the constant address space makes
             // these wave-uniform loads scalar loads.
-            const_u64* pl = (const_u64*)(L.planes + ((int64_t)(mid >= 0 ? mid : 0) * 2 + wr) * 32);
+            const_u64* pl = (const_u64*)(L.planes + ((int64_t)(mid + 1) * 2 + wr) * 32);
             // A 32-key half with no allowed element in this wave's rows (quadrant
             // (query half wr, key half kt) of the mask empty) has only zero
             // weights: its scores, softmax and products are skipped, since they

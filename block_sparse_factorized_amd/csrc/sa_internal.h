@@ -25,7 +25,8 @@ struct DevLayout {
     const uint64_t* masks_t;  // [n_masks][T*T/64]  the same masks transposed:
                               //                    element (r, s): bit s*T+r
     // Block size 64 only: the masks as 64-bit lane masks ("planes") of the
-    // 32x32 MFMA accumulator layout, [n_masks][wave w = 0, 1][register 0..31].
+    // 32x32 MFMA accumulator layout, [1 + n_masks][wave w = 0, 1][register
+    // 0..31]; set 0 is all ones (a full block), mask m is set m + 1.
     //   planes:   bit L of register 16*t + i = element (row 32w + L%32,
     //             key 32t + 8(i/4) + 4(L/32) + i%4)   (lane = query row)
     //   planes_t: bit L of register 16*t + i = element (row 32t + 8(i/4) +
