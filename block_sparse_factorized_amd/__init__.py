@@ -29,4 +29,5 @@ from ._binding import (  # noqa: F401
     sa_layout_destroy,
     sa_layout_export,
     sa_layout_info,
+    sa_layout_set_residue_view,
 )

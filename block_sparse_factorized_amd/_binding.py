@@ -33,7 +33,7 @@ PATTERNS = {
 }
 
 EXPORTED = [
-    "sa_layout_build", "sa_layout_info", "sa_layout_export", "sa_layout_destroy",
+    "sa_layout_build", "sa_layout_info", "sa_layout_export", "sa_layout_set_residue_view", "sa_layout_destroy",
     "sa_fwd", "sa_bwd", "sa_bwd_workspace_size", "sa_bwd_rowterms", "sa_bwd_dkdv", "sa_bwd_dq",
     "sa_status_string", "sa_last_error",
 ]
@@ -58,6 +58,8 @@ def _load():
     lib.sa_layout_info.restype = cint
     lib.sa_layout_export.argtypes = [vp] * 8
     lib.sa_layout_export.restype = cint
+    lib.sa_layout_set_residue_view.argtypes = [vp, cint]
+    lib.sa_layout_set_residue_view.restype = cint
     lib.sa_layout_destroy.argtypes = [vp]
     lib.sa_layout_destroy.restype = None
     lib.sa_fwd.argtypes = [vp, i32, i32, i64, i32, cint, flt, vp, vp, vp, vp, vp, vp]
@@ -102,6 +104,7 @@ class Layout:
     def __init__(self, handle: int, pattern: str, n: int, l: int, c: int, block: int):
         self.handle = ctypes.c_void_p(handle)
         self.pattern, self.n, self.l, self.c, self.block = pattern, n, l, c, block
+        self.residue_view = False
 
     def info(self) -> Dict[str, int]:
         vals = [ctypes.c_int64() for _ in range(4)]
@@ -125,6 +128,13 @@ class Layout:
             out[k] = out[k][:nnz]
         out["mask_words"] = out["mask_words"][:nm]
         return out
+
+    def set_residue_view(self, enable: bool = True) -> "Layout":
+        """Run this strided-B layout's heads as dense causal attentions over
+        the residue classes mod l (see sa_layout_set_residue_view)."""
+        _check(_lib.sa_layout_set_residue_view(self.handle, int(bool(enable))))
+        self.residue_view = bool(enable)
+        return self
 
     def close(self):
         if self.handle is not None and self.handle.value:
@@ -151,6 +161,10 @@ def sa_layout_info(layout: Layout) -> Dict[str, int]:
 
 def sa_layout_export(layout: Layout) -> Dict[str, np.ndarray]:
     return layout.export()
+
+
+def sa_layout_set_residue_view(layout: Layout, enable: bool = True) -> Layout:
+    return layout.set_residue_view(enable)
 
 
 def sa_layout_destroy(layout: Layout) -> None:

@@ -119,28 +119,37 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(const BwdArgs a)
     const int kmode = (modes >> (2 * member)) & 3;
     const int kh = kmode ? kmode - 1 : wr;
     const unsigned qsel = kmode ? 1u << wr : 3u;
-    const int64_t head = (int64_t)bh * a.n * D;
+    // The walked sequence: row m is position r + vl*m of the head (vl = 1,
+    // r = 0 for a plain layout), rs elements apart; rows >= vm are read
+    // clamped, get zero weight and are never written.
+    const int vl = L.vl, vm = L.vm;
+    const int rs = vl * D;
+    const int64_t head = (int64_t)bh * a.n * D + (int64_t)item.r * D;
+    const int64_t lrow0 = (int64_t)bh * a.n + item.r;  // row-term index of row 0
     const unsigned short* Q = (const unsigned short*)a.q + head;
     const unsigned short* dO = (const unsigned short*)a.dout + head;
-    const float* nl2g = a.nl2 + (int64_t)bh * a.n;
-    const float* dlg = a.ndelta + (int64_t)bh * a.n;
+    const float* nl2g = a.nl2 + lrow0;
+    const float* dlg = a.ndelta + lrow0;
     const int k_local = 32 * kh + n32;
-    const int64_t k_row = (int64_t)(kb < 0 ? 0 : kb) * T + k_local;
+    const int k_row = (kb < 0 ? 0 : kb) * T + k_local;
 
     bf16x8 kop[D / 16], vop[D / 16];
     {
-        const unsigned short* K = (const unsigned short*)a.k + head + k_row * D;
-        const unsigned short* V = (const unsigned short*)a.v + head + k_row * D;
+        const uint32_t kr = (uint32_t)(min(k_row, vm - 1) * rs);
+        const unsigned short* K = (const unsigned short*)a.k + head + kr;
+        const unsigned short* V = (const unsigned short*)a.v + head + kr;
 #pragma unroll
         for (int c = 0; c < D / 16; ++c) {
             kop[c] = *(const bf16x8*)(K + 16 * c + 8 * hh);
             vop[c] = *(const bf16x8*)(V + 16 * c + 8 * hh);
         }
     }
-    // (byte offsets from the tile's first element)
+    // Byte offsets of the direct-to-LDS loads from the tile's first row (the
+    // same for every tile but a ragged last one).
     uint32_t goff[NI];
 #pragma unroll
-    for (int u = 0; u < NI; ++u) goff[u] = 2u * (uint32_t)TL::load_src(u, w, lane);
+    for (int u = 0; u < NI; ++u)
+        goff[u] = 2u * (uint32_t)(TL::load_row(u, w, lane) * rs + TL::load_col(u, w, lane));
     int aoff[D / 16];
 #pragma unroll
     for (int c = 0; c < D / 16; ++c) aoff[c] = TL::off(n32, 2 * c + hh);
@@ -160,18 +169,32 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(const BwdArgs a)
     const int nblk = ld_uniform(&L.kgrp_ptr[grp + 1]) - p0;
     const float c2 = a.scale_log2;
 
-    auto issue = [&](int qb, unsigned char* qd, unsigned char* od, float* rd) {
-        const unsigned short* Qt = Q + (int64_t)qb * T * D;
-        const unsigned short* Ot = dO + (int64_t)qb * T * D;
+    // Starts the loads of query tile qb into (qd, od) and returns this lane's
+    // row term for it (wave 0: nl2, wave 1: -D; a padding row gets nl2 =
+    // -inf, so zero weight, and -D = 0), which the caller stores to LDS.
+    auto issue = [&](int qb, unsigned char* qd, unsigned char* od) {
+        const unsigned short* Qt = Q + (int64_t)qb * T * rs;
+        const unsigned short* Ot = dO + (int64_t)qb * T * rs;
+        const int last = vm - 1 - qb * T;  // last valid row of the tile
 #pragma unroll
         for (int u = 0; u < NI; ++u) {
-            __builtin_amdgcn_global_load_lds((glb_void*)sgpr_base_plus(Qt, goff[u]), (lds_void*)(qd + TL::load_dst(u, w)), 16, 0, 0);
-            __builtin_amdgcn_global_load_lds((glb_void*)sgpr_base_plus(Ot, goff[u]), (lds_void*)(od + TL::load_dst(u, w)), 16, 0, 0);
+            uint32_t o = goff[u];
+            if (last < T - 1) {  // ragged: clamp the row
+                const int ln = opaque(lane);
+                o = 2u * (uint32_t)(min(TL::load_row(u, w, ln), last) * rs + TL::load_col(u, w, ln));
+            }
+            __builtin_amdgcn_global_load_lds((glb_void*)sgpr_base_plus(Qt, o), (lds_void*)(qd + TL::load_dst(u, w)), 16, 0, 0);
+            __builtin_amdgcn_global_load_lds((glb_void*)sgpr_base_plus(Ot, o), (lds_void*)(od + TL::load_dst(u, w)), 16, 0, 0);
         }
-        if (w < 2) {  // wave 0: nl2, wave 1: -D
-            const float* src = (w == 0 ? nl2g : dlg) + (int64_t)qb * T + lane;
-            __builtin_amdgcn_global_load_lds((glb_void*)src, (lds_void*)(rd + T * w), 4, 0, 0);
+        float rt = 0.f;
+        if (w < 2) {
+            const int m = qb * T + lane;
+            if (m < vm)
+                rt = (w == 0 ? nl2g : dlg)[(uint32_t)(vl * m)];
+            else
+                rt = w == 0 ? -INFINITY : 0.f;
         }
+        return rt;
     };
 
     int4 st_cur = {0, 0, 0, 0}, st_nxt = {0, 0, 0, 0};
@@ -187,7 +210,8 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(const BwdArgs a)
         // Step records are loaded two steps ahead, so no list read is waited
         // for in the step that uses it.
         const int4 step = st_cur;
-        if (t + 1 < nblk) issue(st_nxt.x, qn, on, rn);
+        float rt_next = 0.f;
+        if (t + 1 < nblk) rt_next = issue(st_nxt.x, qn, on);
         st_cur = st_nxt;
         st_nxt = ld_uniform(&L.kgrp_step[p0 + min(t + 2, nblk - 1)]);
         const int mid = member ? step.z : step.y;  // -2: this key block is not listed
@@ -268,11 +292,15 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(const BwdArgs a)
                         }
                 }
         }  // this wave's key block is listed by the query block
+        if (w < 2 && t + 1 < nblk) rn[T * w + lane] = rt_next;
         wait_vmem();
         __syncthreads();
     };
 
-    if (nblk > 0) issue(st_cur.x, qbuf0, obuf0, rbuf0);
+    if (nblk > 0) {
+        const float rt0 = issue(st_cur.x, qbuf0, obuf0);
+        if (w < 2) rbuf0[T * w + lane] = rt0;
+    }
     wait_vmem();
     __syncthreads();
     for (int t = 0; t < nblk; t += 2) {
@@ -306,21 +334,22 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(const BwdArgs a)
         }
     }
     if (kb < 0) return;
-    // Each wave writes one 32-key half of its block.  In a shared-half member
+    // Each wave writes one 32-key half of its block (its valid rows).  In a shared-half member
     // wave 0 writes the shared half, wave 1 the other half, whose keys no
     // query reaches: zeros.
-    int64_t out_row = k_row;
+    int out_row = k_row;
     if (kmode && wr == 1) {
-        out_row = (int64_t)kb * T + 32 * (1 - kh) + n32;
+        out_row = kb * T + 32 * (1 - kh) + n32;
 #pragma unroll
         for (int dt = 0; dt < D / 32; ++dt) {
             zero(dk[dt]);
             zero(dv[dt]);
         }
     }
+    if (out_row >= vm) return;  // a ragged block's padding row
     // Register i of dk[dt]/dv[dt]: d = 32*dt + 8*(i/4) + 4*hh + i%4 of key out_row.
-    unsigned short* DK = (unsigned short*)a.dk + head + out_row * D;
-    unsigned short* DV = (unsigned short*)a.dv + head + out_row * D;
+    unsigned short* DK = (unsigned short*)a.dk + head + (uint32_t)(out_row * rs);
+    unsigned short* DV = (unsigned short*)a.dv + head + (uint32_t)(out_row * rs);
 #pragma unroll
     for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
@@ -368,28 +397,37 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D == 64 ? 4
     const DevLayout L = a.heads.lay[a.heads.head_lay[bh % a.H]];
     const int2 pair = ld_uniform(&L.qgrp_blk[grp]);
     const int qb = member ? pair.y : pair.x;  // -1: this wave has no rows
-    const int64_t head = (int64_t)bh * a.n * D;
+    // The walked sequence: row m is position r + vl*m of the head (vl = 1,
+    // r = 0 for a plain layout), rs elements apart; rows >= vm are read
+    // clamped and never written.
+    const int vl = L.vl, vm = L.vm;
+    const int rs = vl * D;
+    const int64_t head = (int64_t)bh * a.n * D + (int64_t)item.r * D;
+    const int64_t lrow0 = (int64_t)bh * a.n + item.r;  // row-term index of row 0
     const unsigned short* K = (const unsigned short*)a.k + head;
     const unsigned short* V = (const unsigned short*)a.v + head;
     const int q_local = 32 * wr + n32;
-    const int64_t q_row = (int64_t)(qb < 0 ? 0 : qb) * T + q_local;
+    const int q_row = (qb < 0 ? 0 : qb) * T + q_local;
+    const int q_rc = min(q_row, vm - 1);  // clamped for reads
 
     bf16x8 qop[D / 16], dop[D / 16];
     {
-        const unsigned short* Qr = (const unsigned short*)a.q + head + q_row * D;
-        const unsigned short* Or = (const unsigned short*)a.dout + head + q_row * D;
+        const unsigned short* Qr = (const unsigned short*)a.q + head + (uint32_t)(q_rc * rs);
+        const unsigned short* Or = (const unsigned short*)a.dout + head + (uint32_t)(q_rc * rs);
 #pragma unroll
         for (int c = 0; c < D / 16; ++c) {
             qop[c] = *(const bf16x8*)(Qr + 16 * c + 8 * hh);
             dop[c] = *(const bf16x8*)(Or + 16 * c + 8 * hh);
         }
     }
-    const float nl2 = a.nl2[(int64_t)bh * a.n + q_row];
-    const float nd_i = a.ndelta[(int64_t)bh * a.n + q_row];
-    // (byte offsets from the tile's first element)
+    const float nl2 = a.nl2[lrow0 + (uint32_t)(vl * q_rc)];
+    const float nd_i = a.ndelta[lrow0 + (uint32_t)(vl * q_rc)];
+    // Byte offsets of the direct-to-LDS loads from the tile's first row (the
+    // same for every tile but a ragged last one).
     uint32_t goff[NI];
 #pragma unroll
-    for (int u = 0; u < NI; ++u) goff[u] = 2u * (uint32_t)TL::load_src(u, w, lane);
+    for (int u = 0; u < NI; ++u)
+        goff[u] = 2u * (uint32_t)(TL::load_row(u, w, lane) * rs + TL::load_col(u, w, lane));
     int aoff[D / 16];
 #pragma unroll
     for (int c = 0; c < D / 16; ++c) aoff[c] = TL::off(n32, 2 * c + hh);
@@ -407,12 +445,18 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D == 64 ? 4
     const float c2 = a.scale_log2;
 
     auto issue = [&](int kb, unsigned char* kd, unsigned char* vd) {
-        const unsigned short* Kt = K + (int64_t)kb * T * D;
-        const unsigned short* Vt = V + (int64_t)kb * T * D;
+        const unsigned short* Kt = K + (int64_t)kb * T * rs;
+        const unsigned short* Vt = V + (int64_t)kb * T * rs;
+        const int last = vm - 1 - kb * T;  // last valid row of the tile
 #pragma unroll
         for (int u = 0; u < NI; ++u) {
-            __builtin_amdgcn_global_load_lds((glb_void*)sgpr_base_plus(Kt, goff[u]), (lds_void*)(kd + TL::load_dst(u, w)), 16, 0, 0);
-            __builtin_amdgcn_global_load_lds((glb_void*)sgpr_base_plus(Vt, goff[u]), (lds_void*)(vd + TL::load_dst(u, w)), 16, 0, 0);
+            uint32_t o = goff[u];
+            if (last < T - 1) {  // ragged: clamp the row
+                const int ln = opaque(lane);
+                o = 2u * (uint32_t)(min(TL::load_row(u, w, ln), last) * rs + TL::load_col(u, w, ln));
+            }
+            __builtin_amdgcn_global_load_lds((glb_void*)sgpr_base_plus(Kt, o), (lds_void*)(kd + TL::load_dst(u, w)), 16, 0, 0);
+            __builtin_amdgcn_global_load_lds((glb_void*)sgpr_base_plus(Vt, o), (lds_void*)(vd + TL::load_dst(u, w)), 16, 0, 0);
         }
     };
 
@@ -506,8 +550,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D == 64 ? 4
         if (t + 1 < nblk) step_tile(t + 1, kbuf1, vbuf1, kbuf0, vbuf0);
     }
 
-    if (qb < 0) return;
-    unsigned short* DQ = (unsigned short*)a.dq + head + q_row * D;
+    if (qb < 0 || q_row >= vm) return;  // no rows, or a ragged block's padding row
+    unsigned short* DQ = (unsigned short*)a.dq + head + (uint32_t)(q_row * rs);
 #pragma unroll
     for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll

@@ -194,6 +194,8 @@ int device_layout(sa_layout* L, int dev, DevLayout* out)
     v.kgrp_blk = (const int2*)(b + off_gblk[1]);
     v.kgrp_step = (const int4*)(b + off_gstep[1]);
     v.kgrp_mode = (const int32_t*)(b + off_kmode);
+    v.vl = (int32_t)L->view_l;
+    v.vm = (int32_t)L->view_m;
     L->dev_mem[dev] = mem;
     L->dev[dev] = v;
     *out = v;
@@ -232,17 +234,21 @@ int get_plan(ListKind kind, int dev, int32_t B, int32_t H, sa_layout* const* hl,
         default: return L->kgroups.ptr;
         }
     };
+    // (a residue view walks its dense causal layout once per residue class)
     int64_t count = 0;
-    for (int32_t bh = 0; bh < B * H; ++bh) count += (int64_t)listing(hl[bh % H]).size() - 1;
+    for (int32_t bh = 0; bh < B * H; ++bh)
+        count += ((int64_t)listing(hl[bh % H]).size() - 1) * hl[bh % H]->view_l;
     std::vector<Item> items((size_t)count);
     std::vector<int32_t> cost((size_t)count);
     size_t x = 0;
     for (int32_t bh = 0; bh < B * H; ++bh) {
-        const std::vector<int32_t>& ptr = listing(hl[bh % H]);
-        for (int64_t blk = 0; blk + 1 < (int64_t)ptr.size(); ++blk, ++x) {
-            items[x] = Item{bh, (int32_t)blk};
-            cost[x] = ptr[blk + 1] - ptr[blk];
-        }
+        const sa_layout* L = hl[bh % H];
+        const std::vector<int32_t>& ptr = listing(L);
+        for (int64_t r = 0; r < L->view_l; ++r)
+            for (int64_t blk = 0; blk + 1 < (int64_t)ptr.size(); ++blk, ++x) {
+                items[x] = Item{bh, (int32_t)blk, (int32_t)r, 0};
+                cost[x] = ptr[blk + 1] - ptr[blk];
+            }
     }
     std::vector<size_t> order((size_t)count);
     std::iota(order.begin(), order.end(), 0);
@@ -298,6 +304,7 @@ int common_checks(const char* fn, const sa_layout_t* const* head_layout, int32_t
         if (L->T != block)
             return fail(SA_ERR_UNSUPPORTED, "%s: head_layout[%d] has block %d; %s kernels need block %d", fn, h, L->T,
                         dtype == SA_F32 ? "f32" : "bf16", block);
+        if (L->rview) L = L->rview;  // residue view: the kernels walk its dense causal layout
         int idx = -1;
         for (int a = 0; a < nl; ++a)
             if (distinct[a] == L) idx = a;
@@ -310,9 +317,11 @@ int common_checks(const char* fn, const sa_layout_t* const* head_layout, int32_t
         ht->head_lay[h] = (uint8_t)idx;
         (*hl)[h] = L;
     }
-    if ((int64_t)B * H * (n / block) > (int64_t)1 << 30)
+    int64_t max_items = 0;
+    for (int32_t h = 0; h < H; ++h) max_items += (*hl)[h]->nqb * (*hl)[h]->view_l;
+    if ((int64_t)B * max_items > (int64_t)1 << 30)
         return fail(SA_ERR_UNSUPPORTED, "%s: %lld work items is too many for one launch", fn,
-                    (long long)((int64_t)B * H * (n / block)));
+                    (long long)((int64_t)B * max_items));
     *n_distinct = nl;
     for (int a = 0; a < nl; ++a) distinct_out[a] = distinct[a];
     return SA_OK;
@@ -372,9 +381,38 @@ int sa_layout_export(const sa_layout_t* lay, int32_t* row_ptr, int32_t* col_idx,
     return SA_OK;
 }
 
+int sa_layout_set_residue_view(sa_layout_t* lay, int enable)
+{
+    if (!lay) return fail(SA_ERR_INVALID_ARG, "sa_layout_set_residue_view: layout is NULL");
+    if (!enable) {
+        if (lay->rview) {
+            sa_layout_destroy(lay->rview);
+            lay->rview = nullptr;
+        }
+        return SA_OK;
+    }
+    if (lay->pattern != SA_STRIDED_B)
+        return fail(SA_ERR_UNSUPPORTED, "sa_layout_set_residue_view: only strided B layouts have a residue view");
+    if (lay->T != 64)
+        return fail(SA_ERR_UNSUPPORTED, "sa_layout_set_residue_view: needs block 64 (the bf16 kernels)");
+    if (lay->n % lay->l != 0)
+        return fail(SA_ERR_UNSUPPORTED, "sa_layout_set_residue_view: n = %lld is not a multiple of l = %lld",
+                    (long long)lay->n, (long long)lay->l);
+    if (lay->rview) return SA_OK;
+    const int64_t m = lay->n / lay->l, m_pad = (m + 63) / 64 * 64;
+    sa_layout* rv = nullptr;
+    int st = build_layout(SA_DENSE_CAUSAL, m_pad, 1, 0, 64, &rv);
+    if (st != SA_OK) return st;
+    rv->view_l = lay->l;
+    rv->view_m = m;
+    lay->rview = rv;
+    return SA_OK;
+}
+
 void sa_layout_destroy(sa_layout_t* lay)
 {
     if (!lay) return;
+    if (lay->rview) sa_layout_destroy(lay->rview);
     for (auto& kv : lay->dev_mem) {
         int cur = 0;
         if (hipGetDevice(&cur) == hipSuccess && hipSetDevice(kv.first) == hipSuccess) {

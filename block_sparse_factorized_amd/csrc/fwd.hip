@@ -74,23 +74,33 @@ __global__ __launch_bounds__(256) void fwd_bf16_t64_kernel(const FwdArgs a)
     const DevLayout L = a.heads.lay[a.heads.head_lay[bh % a.H]];
     const int2 pair = ld_uniform(&L.qgrp_blk[grp]);
     const int qb = member ? pair.y : pair.x;  // -1: this wave has no rows
-    const int64_t head = (int64_t)bh * a.n * D;
+    // The walked sequence: row m is position r + vl*m of the head (vl = 1,
+    // r = 0 for a plain layout), rs elements apart; rows >= vm are read
+    // clamped and never written.
+    const int vl = L.vl, vm = L.vm;
+    const int rs = vl * D;
+    const int64_t head = (int64_t)bh * a.n * D + (int64_t)item.r * D;
+    const int64_t lrow0 = (int64_t)bh * a.n + item.r;  // lse index of row 0
     const unsigned short* Q = (const unsigned short*)a.q + head;
     const unsigned short* K = (const unsigned short*)a.k + head;
     const unsigned short* V = (const unsigned short*)a.v + head;
     const int q_local = 32 * wr + n32;
-    const int64_t q_row = (int64_t)(qb < 0 ? 0 : qb) * T + q_local;
+    const int q_row = (qb < 0 ? 0 : qb) * T + q_local;
 
     // Q^T as the B operand of S^T = K Q^T: lane (hh, n) holds d = 16c + 8hh .. +7 of query n.
     bf16x8 qop[D / 16];
+    {
+        const unsigned short* Qr = Q + (uint32_t)(min(q_row, vm - 1) * rs);
 #pragma unroll
-    for (int c = 0; c < D / 16; ++c) qop[c] = *(const bf16x8*)(Q + q_row * D + 16 * c + 8 * hh);
+        for (int c = 0; c < D / 16; ++c) qop[c] = *(const bf16x8*)(Qr + 16 * c + 8 * hh);
+    }
 
-    // Per-thread element offsets of the direct-to-LDS loads (the same for every tile).
-    // (byte offsets from the tile's first element)
+    // Per-thread byte offsets of the direct-to-LDS loads from the tile's
+    // first row (the same for every tile but a ragged last one).
     uint32_t goff[NI];
 #pragma unroll
-    for (int u = 0; u < NI; ++u) goff[u] = 2u * (uint32_t)TL::load_src(u, w, lane);
+    for (int u = 0; u < NI; ++u)
+        goff[u] = 2u * (uint32_t)(TL::load_row(u, w, lane) * rs + TL::load_col(u, w, lane));
     // LDS byte offsets of this lane's K reads (A operand of S^T) and V transposing reads.
     int koff[D / 16];
 #pragma unroll
@@ -116,12 +126,18 @@ __global__ __launch_bounds__(256) void fwd_bf16_t64_kernel(const FwdArgs a)
     const float c2 = a.scale_log2;
 
     auto issue = [&](int kb, unsigned char* kd, unsigned char* vd) {
-        const unsigned short* Kt = K + (int64_t)kb * T * D;
-        const unsigned short* Vt = V + (int64_t)kb * T * D;
+        const unsigned short* Kt = K + (int64_t)kb * T * rs;
+        const unsigned short* Vt = V + (int64_t)kb * T * rs;
+        const int last = vm - 1 - kb * T;  // last valid row of the tile
 #pragma unroll
         for (int u = 0; u < NI; ++u) {
-            __builtin_amdgcn_global_load_lds((glb_void*)sgpr_base_plus(Kt, goff[u]), (lds_void*)(kd + TL::load_dst(u, w)), 16, 0, 0);
-            __builtin_amdgcn_global_load_lds((glb_void*)sgpr_base_plus(Vt, goff[u]), (lds_void*)(vd + TL::load_dst(u, w)), 16, 0, 0);
+            uint32_t o = goff[u];
+            if (last < T - 1) {  // ragged: clamp the row
+                const int ln = opaque(lane);
+                o = 2u * (uint32_t)(min(TL::load_row(u, w, ln), last) * rs + TL::load_col(u, w, ln));
+            }
+            __builtin_amdgcn_global_load_lds((glb_void*)sgpr_base_plus(Kt, o), (lds_void*)(kd + TL::load_dst(u, w)), 16, 0, 0);
+            __builtin_amdgcn_global_load_lds((glb_void*)sgpr_base_plus(Vt, o), (lds_void*)(vd + TL::load_dst(u, w)), 16, 0, 0);
         }
     };
 
@@ -277,8 +293,9 @@ __global__ __launch_bounds__(256) void fwd_bf16_t64_kernel(const FwdArgs a)
 
     if (qb < 0) return;
     const float l_tot = l_run + swap_halves(l_run);
+    if (q_row >= vm) return;  // a ragged block's padding row
     const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-    unsigned short* O = (unsigned short*)a.o + head + q_row * D;
+    unsigned short* O = (unsigned short*)a.o + head + (uint32_t)(q_row * rs);
     // Register i of oacc[dt] holds d = 32*dt + 8*(i/4) + 4*hh + i%4 of query q_row.
 #pragma unroll
     for (int dt = 0; dt < D / 32; ++dt)
@@ -289,8 +306,7 @@ __global__ __launch_bounds__(256) void fwd_bf16_t64_kernel(const FwdArgs a)
             u[1] = bf16_pair(oacc[dt][4 * g + 2] * inv, oacc[dt][4 * g + 3] * inv);
             *(u32x2*)(O + 32 * dt + 8 * g + 4 * hh) = u;
         }
-    if (hh == 0)
-        a.lse[(int64_t)bh * a.n + q_row] = l_tot > 0.f ? m_ref * a.scale + logf(l_tot) : -INFINITY;
+    if (hh == 0) a.lse[lrow0 + (uint32_t)(vl * q_row)] = l_tot > 0.f ? m_ref * a.scale + logf(l_tot) : -INFINITY;
 }
 
 __global__ __launch_bounds__(64) void fwd_f32_t16_d64_kernel(const FwdArgs a)

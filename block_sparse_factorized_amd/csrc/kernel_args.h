@@ -9,13 +9,15 @@
 
 namespace sa {
 
-// One (batch*H + head, block) work item.  blk is a query block for the fp32
-// forward kernel, and an index into the layout's pair lists (query-block
-// pairs for the bf16 forward and dQ kernels, key-block pairs for the dK/dV
-// kernel) otherwise.
+// One (batch*H + head, block, residue) work item.  blk is a query block for
+// the fp32 forward kernel, and an index into the layout's pair lists
+// (query-block pairs for the bf16 forward and dQ kernels, key-block pairs for
+// the dK/dV kernel) otherwise; r is the residue class of a residue view.
 struct Item {
     int32_t bh;
     int32_t blk;
+    int32_t r;    // residue class (0 for a plain layout)
+    int32_t pad;
 };
 
 struct HeadTable {

@@ -200,6 +200,8 @@ int build_layout(int pattern, int64_t n, int64_t l, int64_t c, int32_t block, sa
         L->serial = next_serial();
         L->pattern = pattern;
         L->n = n;
+        L->view_l = 1;
+        L->view_m = n;
         L->l = l;
         L->c = pattern == SA_FIXED_B ? c : 0;
         L->T = block;

@@ -55,6 +55,13 @@ struct DevLayout {
     // 1 + h when the member's whole query list has allowed elements only in
     // its 32-key half h.
     const int32_t* kgrp_mode;
+    // Sequence view.  Row m of the sequence a work item walks is position
+    // r + vl * m of its (batch, head), r the item's residue; rows m >= vm
+    // (a ragged last block) are read clamped and never written.  A plain
+    // layout: vl = 1, vm = n.  The residue view of a strided-B layout
+    // (stride l): vl = l, vm = n / l, walking a dense causal layout.
+    int32_t vl;
+    int32_t vm;
 };
 
 // Host-side pairing of one listing (see DevLayout).
@@ -78,6 +85,14 @@ struct sa_layout {
     std::vector<uint64_t> masks;
     std::vector<int32_t> col_ptr, row_idx, csr_pos;
     sa::Groups qgroups, kgroups;  // pairs by query block / by key block
+    // Sequence view of this layout when walked by the kernels (see
+    // DevLayout): view_l = 1, view_m = n for a plain layout; the internal
+    // dense causal layout behind a residue view has view_l = l, view_m = n/l.
+    int64_t view_l = 1, view_m = 0;
+    // Residue view (strided B only): when set, the kernels run this layout's
+    // heads as l dense causal attentions over the residue classes mod l,
+    // walking `rview` (a dense causal layout on n/l rounded up to blocks).
+    sa_layout* rview = nullptr;
 
     std::mutex mu;                       // guards dev
     std::map<int, void*> dev_mem;        // device id -> allocation

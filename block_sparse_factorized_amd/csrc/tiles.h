@@ -90,6 +90,16 @@ __device__ static inline const void* sgpr_base_plus(const void* base, uint32_t o
     return (const unsigned char*)base + off;
 }
 
+// x, hidden from the optimiser: arithmetic on the result stays where it is
+// written instead of being hoisted out of a loop (and holding registers).
+__device__ static inline int opaque(int x)
+{
+#if defined(__HIP_DEVICE_COMPILE__)  // the constraint names a GPU register class
+    asm volatile("" : "+v"(x));
+#endif
+    return x;
+}
+
 // Two transposing 8-byte LDS reads (ds_read_b64_tr_b16) forming one 8 x bf16 operand.
 __device__ static inline bf16x8 lds_read_tr8(const unsigned char* p0, const unsigned char* p1)
 {
@@ -127,9 +137,15 @@ struct Tile64 {
     // Element offset in the global tile of the 16 bytes lane `lane` loads in load u of wave w.
     __device__ static inline int load_src(int u, int w, int lane)
     {
+        return load_row(u, w, lane) * D + load_col(u, w, lane);
+    }
+    // Its tile row and its first element in that row.
+    __device__ static inline int load_row(int u, int w, int lane) { return (load_dst(u, w) + 16 * lane) / kRow; }
+    __device__ static inline int load_col(int u, int w, int lane)
+    {
         const int byte = load_dst(u, w) + 16 * lane;
         const int r = byte / kRow, pos = (byte % kRow) >> 4;
-        return r * D + ((pos ^ swz(r)) << 3);
+        return (pos ^ swz(r)) << 3;
     }
     // Byte offset of this lane's half (j4 = 0, 1) of a transposing read that
     // yields the 32x32x16 A operand [d = 32*dt + lane%32][sequence index

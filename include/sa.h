@@ -130,6 +130,27 @@ int sa_layout_export(const sa_layout_t* lay, int32_t* row_ptr, int32_t* col_idx,
                      int32_t* mask_id, uint64_t* mask_words, int32_t* col_ptr,
                      int32_t* row_idx, int32_t* csr_pos);
 
+/*
+ * Residue view of a strided-B layout ("Генеративное моделирование с
+ * разреженными трансформерами", "Разреженное внимание": attention along a
+ * column is attention along a row of the transposed matrix).  Under
+ * strided B with stride l, position i attends exactly the earlier positions
+ * of its residue class i mod l, so a head is l independent dense causal
+ * attentions of length n/l over rows r, r+l, r+2l, ...  With the view on,
+ * sa_fwd and the sa_bwd calls run this layout's heads that way: each
+ * residue class as a dense causal attention (blocks of 64 rows taken l rows
+ * apart, a ragged last block padded): at n = 12288, l = 128 that is 384
+ * blocks per head against the raster layout's 9312.  The results are those
+ * of the raster layout (same pairs; only the rounding order differs).  The layout itself (sa_layout_info, sa_layout_export) is
+ * unchanged.  enable = 0 turns the view off.
+ *
+ * Must not be called while an enqueued sa_fwd/sa_bwd uses the layout.
+ * Errors: SA_ERR_INVALID_ARG when lay == NULL; SA_ERR_UNSUPPORTED unless the
+ * pattern is SA_STRIDED_B, the block is 64 (the bf16 kernels) and n is a
+ * multiple of l; SA_ERR_ALLOC when memory runs out.
+ */
+int sa_layout_set_residue_view(sa_layout_t* lay, int enable);
+
 /* Free a layout and its device copies.  NULL is ignored.  The caller must
  * make sure no enqueued sa_fwd/sa_bwd still uses it. */
 void sa_layout_destroy(sa_layout_t* lay);

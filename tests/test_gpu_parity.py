@@ -37,9 +37,10 @@ def layouts_for(patterns, n, block):
     return out
 
 
-def run(inputs, patterns, block, scale, backward):
+def run(inputs, patterns, block, scale, backward, lays=None):
     n = inputs["q"].shape[2]
-    lays = layouts_for(patterns, n, block)
+    if lays is None:
+        lays = layouts_for(patterns, n, block)
     q, k, v = (inputs[t].to(DEV) for t in ("q", "k", "v"))
     o, lse = sa.sa_fwd(q, k, v, lays, scale)
     res = {"o": o, "lse": lse}
@@ -228,6 +229,84 @@ def test_every_output_element_written(pats, n, d):
     for got, want, nm in zip((dq, dk, dv), ref, ("dq", "dk", "dv")):
         assert not torch.isnan(got.float()).any(), nm
         assert torch.equal(got, want), nm
+
+
+# ---------------------------------------------------------------------------
+# Residue view of strided B: the same pairs, walked per residue class.
+
+RESIDUE = [
+    # (head patterns, n, d, note); strided B heads use the residue view
+    ([("strided_b", 16, 1)], 1024, 64, "n/l = 64: whole blocks"),
+    ([("strided_b", 8, 1)], 768, 64, "n/l = 96: ragged last block"),
+    ([("strided_b", 64, 1)], 1536, 64, "n/l = 24: one ragged block"),
+    ([("strided_b", 4, 1)], 1024, 64, "n/l = 256: four blocks"),
+    ([("strided_b", 32, 1)], 2048, 128, "d = 128"),
+    ([("strided_a", 16, 1), ("strided_b", 16, 1), ("fixed_b", 64, 16)], 1024, 64,
+     "raster and residue-view heads in one call"),
+]
+
+
+def residue_layouts(pats, n):
+    lays = layouts_for(pats, n, 64)
+    for (p, _, _), lay in zip(pats, lays):
+        if p == "strided_b" and not lay.residue_view:
+            lay.set_residue_view(True)
+    return lays
+
+
+@pytest.mark.parametrize("case", RESIDUE, ids=[r[3] for r in RESIDUE])
+def test_residue_view_matches_oracle(case):
+    pats, n, d, _ = case
+    H = len(pats)
+    x = workloads.custom_inputs((2, H, n, d), torch.bfloat16, seed=7 * n + d + H)
+    lays = residue_layouts(pats, n)
+    dev = {t: x[t].to(DEV) for t in ("q", "k", "v", "do")}
+    o, lse = sa.sa_fwd(dev["q"], dev["k"], dev["v"], lays, 1.0)
+    dq, dk, dv = sa.sa_bwd(dev["q"], dev["k"], dev["v"], o, lse, dev["do"], lays, 1.0)
+    torch.cuda.synchronize()
+    res = {"o": o.cpu(), "lse": lse.cpu(), "dq": dq.cpu(), "dk": dk.cpu(), "dv": dv.cpu()}
+    for b in range(2):
+        for h in range(H):
+            compare_head(x, res, b, h, pats[h], 1.0, True, fp32=False)
+
+
+def test_residue_view_every_output_written():
+    pats, n, d = [("strided_b", 8, 1), ("strided_a", 8, 1)], 768, 64
+    x = workloads.custom_inputs((2, 2, n, d), torch.bfloat16, seed=99)
+    lays = residue_layouts(pats, n)
+    q, k, v, do = (x[t].to(DEV) for t in ("q", "k", "v", "do"))
+    ref_o, ref_lse = sa.sa_fwd(q, k, v, lays, 1.0)
+    ref = sa.sa_bwd(q, k, v, ref_o, ref_lse, do, lays, 1.0)
+    nan = float("nan")
+    o = torch.full_like(q, nan)
+    lse = torch.full(q.shape[:3], nan, dtype=torch.float32, device=DEV)
+    sa.sa_fwd(q, k, v, lays, 1.0, o=o, lse=lse)
+    dq, dk, dv = (torch.full_like(q, nan) for _ in range(3))
+    sa.sa_bwd(q, k, v, o, lse, do, lays, 1.0, dq=dq, dk=dk, dv=dv)
+    torch.cuda.synchronize()
+    assert torch.equal(o, ref_o) and torch.equal(lse, ref_lse)
+    for got, want, nm in zip((dq, dk, dv), ref, ("dq", "dk", "dv")):
+        assert not torch.isnan(got.float()).any(), nm
+        assert torch.equal(got, want), nm
+
+
+@pytest.mark.parametrize("name", ["img64", "audio"])
+def test_residue_view_full_size_sampled(name):
+    """The workload at full size with its strided-B heads in the residue view."""
+    w = WORKLOADS[name]
+    x = workloads.make_inputs(w)
+    pats = w.head_patterns()
+    lays = residue_layouts(pats, w.n)
+    res = run(x, pats, w.block, 1.0, backward=True, lays=lays)
+    for (b, h) in sample_heads(w.batch, w.heads):
+        rows = kcols = None
+        if w.n > 20000:
+            rng = np.random.default_rng(h)
+            rows = np.unique(np.concatenate([np.arange(0, 64), rng.integers(0, w.n, 64),
+                                             np.arange(w.n - 32, w.n)]))
+            kcols = np.unique(np.concatenate([np.arange(0, 16), rng.integers(0, w.n, 32),
+                                              np.arange(w.n - 16, w.n)]))
+        compare_head(x, res, b, h, pats[h], 1.0, True, fp32=False, rows=rows, kcols=kcols)
 
 
 def test_noncurrent_stream():

@@ -178,6 +178,34 @@ def test_fwd_bwd_argument_errors_without_gpu():
     assert sa.sa_bwd_workspace_size(2, 3, 100, 64) >= 2 * 3 * 100 * 4
 
 
+def test_residue_view_switch():
+    """The residue view is only for strided B with block 64 and l | n; it
+    leaves the layout's own listing unchanged and can be switched off."""
+    lib = sa.library()
+    lay = sa.sa_layout_build("strided_b", 768, 8, block=64)
+    before = lay.export()
+    lay.set_residue_view(True)
+    lay.set_residue_view(True)  # idempotent
+    after = lay.export()
+    for k in before:
+        assert np.array_equal(before[k], after[k]), k
+    lay.set_residue_view(False)
+    lay.set_residue_view(True)
+    cases = [
+        (("strided_a", 768, 8, 1, 64), sa.SA_ERR_UNSUPPORTED),
+        (("fixed_b", 768, 128, 32, 64), sa.SA_ERR_UNSUPPORTED),
+        (("strided_b", 768, 8, 1, 16), sa.SA_ERR_UNSUPPORTED),   # block 16: fp32 kernels
+        (("strided_b", 768, 96 + 1, 1, 64), sa.SA_ERR_UNSUPPORTED),  # l does not divide n
+    ]
+    for (p, n, l, c, T), code in cases:
+        x = sa.sa_layout_build(p, n, l, c, block=T)
+        with pytest.raises(sa.SAError) as e:
+            x.set_residue_view(True)
+        assert e.value.status == code
+        x.set_residue_view(False)  # switching off is always fine
+    assert lib.sa_layout_set_residue_view(None, 1) == sa.SA_ERR_INVALID_ARG
+
+
 def test_more_than_eight_layouts_rejected():
     lib = sa.library()
     lays = [sa.sa_layout_build("strided_a", 128, l, block=64) for l in range(1, 11)]
