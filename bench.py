@@ -37,6 +37,9 @@ def parse():
     ap.add_argument("--workload", default="img64",
                     help="tiny | img32 | text | img64 | audio (default img64, N=12288)")
     ap.add_argument("--dense", action="store_true", help="run the dense causal comparison layout")
+    ap.add_argument("--residue-view", action="store_true",
+                    help="run strided-B heads in their residue view (a dense causal attention per residue "
+                         "class mod l); the metric then counts the residue view's blocks")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-heads", type=int, default=0,
                     help="heads in the oracle sample (default: sized to ~10-30 s)")
@@ -73,9 +76,25 @@ def traffic_from_profile(kernel_file, kernel, workload):
     return None
 
 
+def residue_blocks(lay):
+    """(blocks per residue class, residue classes) of a residue view: a dense
+    causal attention over n/l rows in blocks of 64."""
+    nb = -(-(lay.n // lay.l) // 64)
+    return nb, lay.l
+
+
+def listed_blocks(lay):
+    """Blocks the kernels walk for one head: the layout's listing, or the
+    residue view's dense causal blocks over every residue class."""
+    if getattr(lay, "residue_view", False):
+        nb, nr = residue_blocks(lay)
+        return nr * nb * (nb + 1) // 2
+    return lay.info()["nnz"]
+
+
 def counted_flops(layouts, batch, T, d):
-    """Forward flops counted over allowed blocks, summed over (batch, head)."""
-    blocks = sum(lay.info()["nnz"] for lay in layouts) * batch
+    """Forward flops counted over the listed blocks, summed over (batch, head)."""
+    blocks = sum(listed_blocks(lay) for lay in layouts) * batch
     return blocks * 4.0 * T * T * d, blocks
 
 
@@ -87,6 +106,10 @@ def live_quadrants(layouts, batch, T):
     import numpy as np
     total = 0
     for lay in layouts:
+        if getattr(lay, "residue_view", False):
+            nb, nr = residue_blocks(lay)  # dense causal: 3 live quadrants on the diagonal
+            total += nr * (3 * nb + 4 * (nb * (nb - 1) // 2))
+            continue
         ex = lay.export()
         mid = np.asarray(ex["mask_id"])
         if T != 64:  # only block-64 kernels skip quadrants
@@ -104,13 +127,12 @@ def live_quadrants(layouts, batch, T):
     return total * batch
 
 
-def cpu_baseline(w, x, pats, T, max_heads):
+def cpu_baseline(w, x, pats, lays, T, max_heads):
     """The fp64 oracle on the host's cores over a bounded sample of heads of
-    the same workload, fwd + bwd, scaled to the same counted-flop metric."""
-    import numpy as np
+    the same workload, fwd + bwd, scaled to the same counted-flop metric
+    (blocks counted as for the GPU run)."""
     import oracle
     from workloads import to_f64
-    import block_sparse_factorized_amd as sa
 
     sample = []
     for b in range(w.batch):
@@ -128,8 +150,7 @@ def cpu_baseline(w, x, pats, T, max_heads):
             oracle.head_bwd(p, l, c, *args, 1.0)
         else:
             oracle.head_fwd(p, l, c, *args[:3], 1.0)
-        lay = sa.sa_layout_build(p, w.n, l, c, block=T)
-        counted += lay.info()["nnz"] * 4.0 * T * T * w.d * (3.5 if w.backward else 1.0)
+        counted += listed_blocks(lays[h]) * 4.0 * T * T * w.d * (3.5 if w.backward else 1.0)
     secs = time.perf_counter() - t0
     return {
         "value": counted / secs / 1e12,
@@ -167,9 +188,12 @@ def main():
     for (p, l, c) in pats:
         if (p, l, c) not in cache:
             cache[(p, l, c)] = sa.sa_layout_build(p, w.n, l, c, block=T)
+            if args.residue_view and p == "strided_b":
+                cache[(p, l, c)].set_residue_view(True)
         lays.append(cache[(p, l, c)])
     layout_ms = (time.perf_counter() - t0) * 1e3
 
+    label = w.name + ("-dense" if args.dense else "") + ("-residue-view" if args.residue_view else "")
     x = workloads.make_inputs(w)
     q, k, v, do = (x[t].to(dev) for t in ("q", "k", "v", "do"))
     o = torch.empty_like(q)
@@ -248,7 +272,7 @@ def main():
         "peak": peak,
         "unit": "TFLOP/s",
         "frac": dk_["tflops"] / peak,
-        "traffic": traffic_from_profile(kern_file, kern_sym[dominant], w.name + ("-dense" if args.dense else "")),
+        "traffic": traffic_from_profile(kern_file, kern_sym[dominant], label),
         "counted_flops_per_launch": dk_["counted_gflop"] * 1e9,
         "avg_launch_us": dk_["avg_us"],
         # What the matrix cores actually execute (empty quadrants skipped).
@@ -269,12 +293,18 @@ def main():
         "dtype": w.dtype,
         "data": "synthetic",
         "config": {
-            "workload": w.name + ("-dense" if args.dense else ""),
+            "workload": label,
             "batch": w.batch, "heads": w.heads, "n": w.n, "head_dim": d, "block": T,
             "pattern": "dense causal" if args.dense else w.pattern, "l": w.l, "c": w.c,
             "scale": scale, "allowed_blocks": blocks, "backward": w.backward,
+            "residue_view": bool(args.residue_view),
         },
         "frac_of_peak": value / peak,
+        # With the residue view, the raster layouts' block count over the same
+        # step time (a reference only: the residue view walks fewer blocks).
+        "raster_counted_tflops": (sum(lay.info()["nnz"] for lay in lays) * w.batch * 4.0 * T * T * d
+                                  * (3.5 if w.backward else 1.0) / (ms_per_step * 1e-3) / 1e12)
+        if args.residue_view else None,
         "live_quadrant_fraction": quads / (4.0 * blocks) if blocks else None,
         "kernels": kernels,
         "fwd_frac_of_peak": kernels["fwd"]["tflops"] / peak,
@@ -284,7 +314,7 @@ def main():
     }
     if not args.no_cpu_baseline:
         heads = args.cpu_heads or {"tiny": 2, "img32": 16, "text": 16, "img64": 32, "audio": 2}[w.name]
-        out["cpu_baseline"] = cpu_baseline(w, x, pats, T, heads)
+        out["cpu_baseline"] = cpu_baseline(w, x, pats, lays, T, heads)
     print(json.dumps(out), flush=True)
 
 
