@@ -43,6 +43,9 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-heads", type=int, default=0,
                     help="heads in the oracle sample (default: sized to ~10-30 s)")
+    ap.add_argument("--length-scaling", action="store_true",
+                    help="time fwd and fwd+bwd for n = 2^12 .. 2^20 with strided heads of stride l = sqrt(n) "
+                         "(head A raster, head B in its residue view) and fit the exponent of n")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 512 MiB device copy 5 times (to scale HBM counters)")
     return ap.parse_args()
@@ -162,6 +165,69 @@ def cpu_baseline(w, x, pats, lays, T, max_heads):
     }
 
 
+def length_scaling(args):
+    """Step time against sequence length for the strided pattern with
+    l = sqrt(n): the pages' O(n sqrt n) cost (batch 1, one head of each of
+    strided A and B, d = 64, bf16, scale 1).  One JSON line."""
+    import numpy as np
+    import torch
+    import block_sparse_factorized_amd as sa
+    import workloads
+
+    dev = torch.device("cuda:0")
+    points = []
+    for k in (12, 14, 16, 18, 20):
+        n, l, d = 1 << k, 1 << (k // 2), 64
+        a = sa.sa_layout_build("strided_a", n, l, block=64)
+        b = sa.sa_layout_build("strided_b", n, l, block=64).set_residue_view(True)
+        lays = [a, b]
+        x = workloads.custom_inputs((1, 2, n, d), torch.bfloat16, seed=k)
+        q, kk, v, do = (x[t].to(dev) for t in ("q", "k", "v", "do"))
+        del x
+        o = torch.empty_like(q)
+        lse = torch.empty(q.shape[:3], dtype=torch.float32, device=dev)
+        dq, dk, dv = torch.empty_like(q), torch.empty_like(q), torch.empty_like(q)
+        ws = torch.empty(sa.sa_bwd_workspace_size(1, 2, n, d), dtype=torch.uint8, device=dev)
+        reps = max(3, min(args.steps, 20))
+
+        def timed(fn):
+            for _ in range(2):
+                fn()
+            ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+            torch.cuda.synchronize()
+            ev[0].record()
+            for _ in range(reps):
+                fn()
+            ev[1].record()
+            torch.cuda.synchronize()
+            return ev[0].elapsed_time(ev[1]) / reps
+
+        fwd_ms = timed(lambda: sa.sa_fwd(q, kk, v, lays, 1.0, o=o, lse=lse))
+        step_ms = timed(lambda: (sa.sa_fwd(q, kk, v, lays, 1.0, o=o, lse=lse),
+                                 sa.sa_bwd(q, kk, v, o, lse, do, lays, 1.0, dq=dq, dk=dk, dv=dv, workspace=ws)))
+        pairs = a.info()["allowed"] + b.info()["allowed"]
+        points.append({"n": n, "l": l, "allowed_pairs": pairs, "fwd_ms": fwd_ms, "fwd_bwd_ms": step_ms,
+                       "blocks_walked": listed_blocks(a) + listed_blocks(b)})
+        print("n = %d: fwd %.3f ms, fwd+bwd %.3f ms" % (n, fwd_ms, step_ms), file=sys.stderr, flush=True)
+        del q, kk, v, do, o, lse, dq, dk, dv, ws
+        torch.cuda.empty_cache()
+    # Exponent of n between consecutive lengths (the small ones do not fill
+    # the GPU, so the exponent approaches the pages' 1.5 only at large n).
+    local = []
+    for p1, p2 in zip(points, points[1:]):
+        e = lambda key: float(np.log(p2[key] / p1[key]) / np.log(p2["n"] / p1["n"]))
+        local.append({"n_from": p1["n"], "n_to": p2["n"], "pairs": e("allowed_pairs"), "fwd": e("fwd_ms"),
+                      "fwd_bwd": e("fwd_bwd_ms")})
+    print(json.dumps({
+        "metric": "step time vs sequence length, strided heads with l = sqrt(n)",
+        "unit": "ms", "higher_is_better": False, "n_gpus": 1, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "length-scaling", "batch": 1, "heads": 2, "head_dim": 64, "block": 64,
+                   "pattern": "strided A (raster) + strided B (residue view), l = sqrt(n)"},
+        "points": points,
+        "local_exponents": local,
+    }), flush=True)
+
+
 def main():
     args = parse()
     if args.copy_calibration:
@@ -171,6 +237,10 @@ def main():
         print("bench.py runs on one GPU only: this build has no multi-GPU path "
               "(--gpus %d refused)" % args.gpus, file=sys.stderr)
         sys.exit(2)
+
+    if args.length_scaling:
+        length_scaling(args)
+        return
 
     import numpy as np
     import torch
