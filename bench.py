@@ -46,6 +46,9 @@ def parse():
     ap.add_argument("--length-scaling", action="store_true",
                     help="time fwd and fwd+bwd for n = 2^12 .. 2^20 with strided heads of stride l = sqrt(n) "
                          "(head A raster, head B in its residue view) and fit the exponent of n")
+    ap.add_argument("--memory", action="store_true",
+                    help="64 stacked layers of 4-head attention at n = 12288 through the autograd wrapper: "
+                         "memory kept for the backward pass against dense n x n weights")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 512 MiB device copy 5 times (to scale HBM counters)")
     return ap.parse_args()
@@ -228,6 +231,55 @@ def length_scaling(args):
     }), flush=True)
 
 
+def memory_run(args):
+    """Memory kept for the backward pass by 64 stacked self-attention layers
+    (the pages' 154 GB example: 64 layers, 4 heads, n = 12288, stored
+    attention weights in fp32 would take 64 * 4 * 12288^2 * 4 bytes), run
+    through sparse_attention, which keeps only O and lse per layer.  One
+    JSON line."""
+    import torch
+    import block_sparse_factorized_amd as sa
+    import workloads
+
+    dev = torch.device("cuda:0")
+    layers, B, H, n, d, l = 64, 1, 4, 12288, 64, 128
+    pats = [("strided_a", l, 1), ("strided_b", l, 1)] * (H // 2)
+    lay_a, lay_b = sa.sa_layout_build("strided_a", n, l, block=64), sa.sa_layout_build("strided_b", n, l, block=64)
+    lays = [lay_a, lay_b] * (H // 2)
+    x0 = workloads.custom_inputs((B, H, n, d), torch.bfloat16, seed=64, with_dout=False)["q"].to(dev)
+    x0.requires_grad_(True)
+    torch.cuda.synchronize()
+    torch.cuda.reset_peak_memory_stats(dev)
+    base = torch.cuda.memory_allocated(dev)
+    t0 = time.perf_counter()
+    x = x0
+    for _ in range(layers):
+        x = sa.sparse_attention(x, x, x, lays, 1.0)  # self-attention, no projections
+    torch.cuda.synchronize()
+    t_fwd = time.perf_counter() - t0
+    kept = torch.cuda.memory_allocated(dev) - base
+    t0 = time.perf_counter()
+    x.backward(torch.ones_like(x))
+    torch.cuda.synchronize()
+    t_bwd = time.perf_counter() - t0
+    peak = torch.cuda.max_memory_allocated(dev) - base
+    act = B * H * n * d * 2              # one layer's output (bf16)
+    lse = B * H * n * 4                  # its log-sum-exp (fp32)
+    dense = B * H * n * n * 4            # its attention weights, fp32
+    print(json.dumps({
+        "metric": "memory kept for the backward pass, 64 layers of 4-head attention at n = 12288",
+        "unit": "bytes", "higher_is_better": False, "n_gpus": 1, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "memory-64-layers", "layers": layers, "batch": B, "heads": H, "n": n,
+                   "head_dim": d, "patterns": "strided A/B, l = 128", "block": 64},
+        "kept_bytes": kept, "kept_bytes_per_layer": kept / layers,
+        "expected_per_layer_output_plus_lse": act + lse,
+        "peak_bytes_fwd_bwd": peak,
+        "dense_weights_bytes_per_layer": dense, "dense_weights_bytes_total": dense * layers,
+        "dense_over_kept": dense * layers / kept if kept else None,
+        "fwd_s": t_fwd, "bwd_s": t_bwd,
+    }), flush=True)
+
+
 def main():
     args = parse()
     if args.copy_calibration:
@@ -240,6 +292,9 @@ def main():
 
     if args.length_scaling:
         length_scaling(args)
+        return
+    if args.memory:
+        memory_run(args)
         return
 
     import numpy as np

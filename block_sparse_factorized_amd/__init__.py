@@ -30,4 +30,5 @@ from ._binding import (  # noqa: F401
     sa_layout_export,
     sa_layout_info,
     sa_layout_set_residue_view,
+    sparse_attention,
 )

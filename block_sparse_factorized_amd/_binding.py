@@ -248,6 +248,40 @@ def sa_bwd(q, k, v, o, lse, do, layouts: Union[Layout, Sequence[Layout]], scale:
     return dq, dk, dv
 
 
+def sparse_attention(q, k, v, layouts: Union[Layout, Sequence[Layout]], scale: float):
+    """O = attention over the layouts' allowed pairs, differentiable in q, k
+    and v.  Only O and lse are kept for the backward pass, which recomputes
+    the attention weights block by block (sa_bwd); no n x n matrix is ever
+    stored."""
+    return _sparse_attention_fn().apply(q, k, v, layouts, float(scale))
+
+
+_SPARSE_ATTENTION_FN = None
+
+
+def _sparse_attention_fn():
+    global _SPARSE_ATTENTION_FN
+    if _SPARSE_ATTENTION_FN is None:
+        import torch
+
+        class SparseAttention(torch.autograd.Function):
+            @staticmethod
+            def forward(ctx, q, k, v, layouts, scale):
+                o, lse = sa_fwd(q, k, v, layouts, scale)
+                ctx.save_for_backward(q, k, v, o, lse)
+                ctx.layouts, ctx.scale = layouts, scale
+                return o
+
+            @staticmethod
+            def backward(ctx, do):
+                q, k, v, o, lse = ctx.saved_tensors
+                dq, dk, dv = sa_bwd(q, k, v, o, lse, do.contiguous(), ctx.layouts, ctx.scale)
+                return dq, dk, dv, None, None
+
+        _SPARSE_ATTENTION_FN = SparseAttention
+    return _SPARSE_ATTENTION_FN
+
+
 def _bwd_common(q, layouts, workspace):
     import torch
     B, H, n, d = q.shape

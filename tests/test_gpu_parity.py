@@ -309,6 +309,28 @@ def test_residue_view_full_size_sampled(name):
         compare_head(x, res, b, h, pats[h], 1.0, True, fp32=False, rows=rows, kcols=kcols)
 
 
+def test_autograd_wrapper_recomputes():
+    """sparse_attention's gradients are sa_bwd's, bit for bit, and the only
+    tensors it keeps besides q, k, v are O and lse (no n x n weights)."""
+    pats, n, d = [("strided_a", 64, 1), ("strided_b", 64, 1)], 1024, 64
+    x = workloads.custom_inputs((2, 2, n, d), torch.bfloat16, seed=123)
+    lays = layouts_for(pats, n, 64)
+    q, k, v, do = (x[t].to(DEV) for t in ("q", "k", "v", "do"))
+    qg, kg, vg = (t.clone().requires_grad_(True) for t in (q, k, v))
+    o = sa.sparse_attention(qg, kg, vg, lays, 1.0)
+    saved = o.grad_fn.saved_tensors
+    assert len(saved) == 5
+    assert sum(t.numel() * t.element_size() for t in saved[3:]) == (
+        o.numel() * o.element_size() + 2 * 2 * n * 4)  # O and lse only
+    o.backward(do)
+    ref_o, ref_lse = sa.sa_fwd(q, k, v, lays, 1.0)
+    ref = sa.sa_bwd(q, k, v, ref_o, ref_lse, do, lays, 1.0)
+    torch.cuda.synchronize()
+    assert torch.equal(o.detach(), ref_o)
+    for g, r, nm in zip((qg.grad, kg.grad, vg.grad), ref, ("dq", "dk", "dv")):
+        assert torch.equal(g, r), nm
+
+
 def test_noncurrent_stream():
     """Kernels run on the stream they are given."""
     n = 512
