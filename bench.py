@@ -40,6 +40,9 @@ def parse():
     ap.add_argument("--residue-view", action="store_true",
                     help="run strided-B heads in their residue view (a dense causal attention per residue "
                          "class mod l); the metric then counts the residue view's blocks")
+    ap.add_argument("--compact-view", action="store_true",
+                    help="run fixed-B heads in their compact view (blocks of the summary keys only); the "
+                         "metric then counts the compact view's blocks")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-heads", type=int, default=0,
                     help="heads in the oracle sample (default: sized to ~10-30 s)")
@@ -90,12 +93,34 @@ def residue_blocks(lay):
 
 
 def listed_blocks(lay):
-    """Blocks the kernels walk for one head: the layout's listing, or the
-    residue view's dense causal blocks over every residue class."""
-    if getattr(lay, "residue_view", False):
-        nb, nr = residue_blocks(lay)
-        return nr * nb * (nb + 1) // 2
-    return lay.info()["nnz"]
+    """Blocks the kernels walk for one head: the layout's listing, the
+    residue view's dense causal blocks over every residue class, or the
+    compact view's blocks."""
+    v = lay.view_info()
+    return v["nnz"] * (lay.l if v["kind"] == "residue" else 1)
+
+
+def listed_blocks_dkdv(lay):
+    """Blocks the dK/dV kernel walks for one head: as listed_blocks, but a
+    compact view's heads in their raster layout (that kernel does not walk
+    compact views)."""
+    v = lay.view_info()
+    return lay.info()["nnz"] if v["kind"] == "compact" else listed_blocks(lay)
+
+
+def compact_live_quadrants(lay):
+    """Live 32 x 32 quadrants of a fixed-B compact view: query row i sees the
+    first cnt(i) summary keys, so quadrant (query half rh, key half ch) of
+    block (qb, kb) is live when some row of half rh has cnt > 64 kb + 32 ch."""
+    import numpy as np
+    n, l, c = lay.n, lay.l, lay.c
+    i = np.arange(n, dtype=np.int64)
+    cnt = (i + 1) // l * c + np.maximum(0, (i + 1) % l - (l - c))
+    half_max = cnt.reshape(-1, 32).max(1)  # widest row of every 32-row half
+    nkb = -(-(n // l * c) // 64)
+    kb = np.arange(nkb, dtype=np.int64)
+    live = half_max[:, None, None] > (64 * kb[None, :, None] + 32 * np.arange(2)[None, None, :])
+    return int(live.sum())
 
 
 def counted_flops(layouts, batch, T, d):
@@ -104,7 +129,7 @@ def counted_flops(layouts, batch, T, d):
     return blocks * 4.0 * T * T * d, blocks
 
 
-def live_quadrants(layouts, batch, T):
+def live_quadrants(layouts, batch, T, raster_compact=False):
     """32 x 32 quadrants of the listed blocks that hold an allowed element,
     summed over (batch, head).  The block-64 kernels skip the others, so
     their matrix cores execute this many quadrants' products; the counted
@@ -115,6 +140,9 @@ def live_quadrants(layouts, batch, T):
         if getattr(lay, "residue_view", False):
             nb, nr = residue_blocks(lay)  # dense causal: 3 live quadrants on the diagonal
             total += nr * (3 * nb + 4 * (nb * (nb - 1) // 2))
+            continue
+        if getattr(lay, "compact_view", False) and not raster_compact:
+            total += compact_live_quadrants(lay)
             continue
         ex = lay.export()
         mid = np.asarray(ex["mask_id"])
@@ -315,10 +343,14 @@ def main():
             cache[(p, l, c)] = sa.sa_layout_build(p, w.n, l, c, block=T)
             if args.residue_view and p == "strided_b":
                 cache[(p, l, c)].set_residue_view(True)
+            if args.compact_view and p == "fixed_b":
+                cache[(p, l, c)].set_compact_view(True)
         lays.append(cache[(p, l, c)])
     layout_ms = (time.perf_counter() - t0) * 1e3
 
-    label = w.name + ("-dense" if args.dense else "") + ("-residue-view" if args.residue_view else "")
+    label = (w.name + ("-dense" if args.dense else "") + ("-residue-view" if args.residue_view else "")
+             + ("-compact-view" if args.compact_view else ""))
+    views = args.residue_view or args.compact_view
     x = workloads.make_inputs(w)
     q, k, v, do = (x[t].to(dev) for t in ("q", "k", "v", "do"))
     o = torch.empty_like(q)
@@ -371,13 +403,17 @@ def main():
     # Matrix-core flops the kernels execute, per live 32 x 32 quadrant
     # (forward S, PV; dK/dV S, dP, dV, dK; dQ S, dP, dQ).
     # The fp32 block-16 kernel skips nothing: it executes what is counted.
+    # (The dK/dV kernel walks compact-view heads in their raster layout.)
     quads = live_quadrants(lays, w.batch, T)
+    quads_kv = live_quadrants(lays, w.batch, T, raster_compact=True) if args.compact_view else quads
+    blocks_kv = sum(listed_blocks_dkdv(lay) for lay in lays) * w.batch
     per_quad = {"fwd": 4.0, "bwd_dkdv": 8.0, "bwd_dq": 6.0, "bwd_rowterms": 0.0}
     kernels = {}
     for nm in names:
         avg_s = float(kernel_ms[nm].mean()) * 1e-3
-        fl = per_block[nm] * T * T * d * blocks
-        ex = per_quad[nm] * 32 * 32 * d * quads if T == 64 else fl
+        nb, nq = (blocks_kv, quads_kv) if nm == "bwd_dkdv" else (blocks, quads)
+        fl = per_block[nm] * T * T * d * nb
+        ex = per_quad[nm] * 32 * 32 * d * nq if T == 64 else fl
         kernels[nm] = {"avg_us": avg_s * 1e6, "median_us": float(np.median(kernel_ms[nm])) * 1e3,
                        "counted_gflop": fl / 1e9, "tflops": fl / avg_s / 1e12 if fl else None,
                        "executed_gflop": ex / 1e9, "executed_tflops": ex / avg_s / 1e12 if ex else None}
@@ -423,13 +459,14 @@ def main():
             "pattern": "dense causal" if args.dense else w.pattern, "l": w.l, "c": w.c,
             "scale": scale, "allowed_blocks": blocks, "backward": w.backward,
             "residue_view": bool(args.residue_view),
+            "compact_view": bool(args.compact_view),
         },
         "frac_of_peak": value / peak,
-        # With the residue view, the raster layouts' block count over the same
-        # step time (a reference only: the residue view walks fewer blocks).
+        # With a residue or compact view, the raster layouts' block count over
+        # the same step time (a reference only: the views walk fewer blocks).
         "raster_counted_tflops": (sum(lay.info()["nnz"] for lay in lays) * w.batch * 4.0 * T * T * d
                                   * (3.5 if w.backward else 1.0) / (ms_per_step * 1e-3) / 1e12)
-        if args.residue_view else None,
+        if views else None,
         "live_quadrant_fraction": quads / (4.0 * blocks) if blocks else None,
         "kernels": kernels,
         "fwd_frac_of_peak": kernels["fwd"]["tflops"] / peak,

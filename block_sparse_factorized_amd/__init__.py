@@ -29,6 +29,8 @@ from ._binding import (  # noqa: F401
     sa_layout_destroy,
     sa_layout_export,
     sa_layout_info,
+    sa_layout_set_compact_view,
     sa_layout_set_residue_view,
+    sa_layout_view_info,
     sparse_attention,
 )

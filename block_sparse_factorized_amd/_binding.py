@@ -33,7 +33,8 @@ PATTERNS = {
 }
 
 EXPORTED = [
-    "sa_layout_build", "sa_layout_info", "sa_layout_export", "sa_layout_set_residue_view", "sa_layout_destroy",
+    "sa_layout_build", "sa_layout_info", "sa_layout_export", "sa_layout_set_residue_view",
+    "sa_layout_set_compact_view", "sa_layout_view_info", "sa_layout_destroy",
     "sa_fwd", "sa_bwd", "sa_bwd_workspace_size", "sa_bwd_rowterms", "sa_bwd_dkdv", "sa_bwd_dq",
     "sa_status_string", "sa_last_error",
 ]
@@ -60,6 +61,10 @@ def _load():
     lib.sa_layout_export.restype = cint
     lib.sa_layout_set_residue_view.argtypes = [vp, cint]
     lib.sa_layout_set_residue_view.restype = cint
+    lib.sa_layout_set_compact_view.argtypes = [vp, cint]
+    lib.sa_layout_set_compact_view.restype = cint
+    lib.sa_layout_view_info.argtypes = [vp, ctypes.POINTER(cint)] + [ctypes.POINTER(i64)] * 4
+    lib.sa_layout_view_info.restype = cint
     lib.sa_layout_destroy.argtypes = [vp]
     lib.sa_layout_destroy.restype = None
     lib.sa_fwd.argtypes = [vp, i32, i32, i64, i32, cint, flt, vp, vp, vp, vp, vp, vp]
@@ -105,6 +110,7 @@ class Layout:
         self.handle = ctypes.c_void_p(handle)
         self.pattern, self.n, self.l, self.c, self.block = pattern, n, l, c, block
         self.residue_view = False
+        self.compact_view = False
 
     def info(self) -> Dict[str, int]:
         vals = [ctypes.c_int64() for _ in range(4)]
@@ -136,6 +142,22 @@ class Layout:
         self.residue_view = bool(enable)
         return self
 
+    def set_compact_view(self, enable: bool = True) -> "Layout":
+        """Run this fixed-B layout's heads against blocks of its summary keys
+        only (see sa_layout_set_compact_view)."""
+        _check(_lib.sa_layout_set_compact_view(self.handle, int(bool(enable))))
+        self.compact_view = bool(enable)
+        return self
+
+    def view_info(self) -> Dict[str, int]:
+        """What the kernels walk for this layout (see sa_layout_view_info)."""
+        kind = ctypes.c_int()
+        vals = [ctypes.c_int64() for _ in range(4)]
+        _check(_lib.sa_layout_view_info(self.handle, ctypes.byref(kind), *[ctypes.byref(v) for v in vals]))
+        out = dict(zip(["nqb", "nkb", "nnz", "allowed"], [v.value for v in vals]))
+        out["kind"] = ("layout", "residue", "compact")[kind.value]
+        return out
+
     def close(self):
         if self.handle is not None and self.handle.value:
             _lib.sa_layout_destroy(self.handle)
@@ -165,6 +187,14 @@ def sa_layout_export(layout: Layout) -> Dict[str, np.ndarray]:
 
 def sa_layout_set_residue_view(layout: Layout, enable: bool = True) -> Layout:
     return layout.set_residue_view(enable)
+
+
+def sa_layout_set_compact_view(layout: Layout, enable: bool = True) -> Layout:
+    return layout.set_compact_view(enable)
+
+
+def sa_layout_view_info(layout: Layout) -> Dict[str, int]:
+    return layout.view_info()
 
 
 def sa_layout_destroy(layout: Layout) -> None:

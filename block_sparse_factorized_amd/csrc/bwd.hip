@@ -121,7 +121,8 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(const BwdArgs a)
     const unsigned qsel = kmode ? 1u << wr : 3u;
     // The walked sequence: row m is position r + vl*m of the head (vl = 1,
     // r = 0 for a plain layout), rs elements apart; rows >= vm are read
-    // clamped, get zero weight and are never written.
+    // clamped, get zero weight and are never written.  (Never a compact
+    // view: its key rows are not remapped here.)
     const int vl = L.vl, vm = L.vm;
     const int rs = vl * D;
     const int64_t head = (int64_t)bh * a.n * D + (int64_t)item.r * D;
@@ -399,8 +400,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D == 64 ? 4
     const int qb = member ? pair.y : pair.x;  // -1: this wave has no rows
     // The walked sequence: row m is position r + vl*m of the head (vl = 1,
     // r = 0 for a plain layout), rs elements apart; rows >= vm are read
-    // clamped and never written.
-    const int vl = L.vl, vm = L.vm;
+    // clamped and never written.  Key t is row key_pos(t) of it; keys >= km
+    // are read clamped (and masked out).
+    const int vl = L.vl, vm = L.vm, km = L.km;
     const int rs = vl * D;
     const int64_t head = (int64_t)bh * a.n * D + (int64_t)item.r * D;
     const int64_t lrow0 = (int64_t)bh * a.n + item.r;  // row-term index of row 0
@@ -427,7 +429,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D == 64 ? 4
     uint32_t goff[NI];
 #pragma unroll
     for (int u = 0; u < NI; ++u)
-        goff[u] = 2u * (uint32_t)(TL::load_row(u, w, lane) * rs + TL::load_col(u, w, lane));
+        goff[u] = 2u * (uint32_t)((key_pos(L, TL::load_row(u, w, lane)) - L.koff) * rs + TL::load_col(u, w, lane));
     int aoff[D / 16];
 #pragma unroll
     for (int c = 0; c < D / 16; ++c) aoff[c] = TL::off(n32, 2 * c + hh);
@@ -445,15 +447,17 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D == 64 ? 4
     const float c2 = a.scale_log2;
 
     auto issue = [&](int kb, unsigned char* kd, unsigned char* vd) {
-        const unsigned short* Kt = K + (int64_t)kb * T * rs;
-        const unsigned short* Vt = V + (int64_t)kb * T * rs;
-        const int last = vm - 1 - kb * T;  // last valid row of the tile
+        const int64_t kr = (int64_t)key_pos(L, kb * T) * rs;
+        const unsigned short* Kt = K + kr;
+        const unsigned short* Vt = V + kr;
+        const int last = km - 1 - kb * T;  // last valid key of the tile
 #pragma unroll
         for (int u = 0; u < NI; ++u) {
             uint32_t o = goff[u];
-            if (last < T - 1) {  // ragged: clamp the row
+            if (last < T - 1) {  // ragged: clamp the key
                 const int ln = opaque(lane);
-                o = 2u * (uint32_t)(min(TL::load_row(u, w, ln), last) * rs + TL::load_col(u, w, ln));
+                o = 2u * (uint32_t)((key_pos(L, min(TL::load_row(u, w, ln), last)) - L.koff) * rs +
+                                    TL::load_col(u, w, ln));
             }
             __builtin_amdgcn_global_load_lds((glb_void*)sgpr_base_plus(Kt, o), (lds_void*)(kd + TL::load_dst(u, w)), 16, 0, 0);
             __builtin_amdgcn_global_load_lds((glb_void*)sgpr_base_plus(Vt, o), (lds_void*)(vd + TL::load_dst(u, w)), 16, 0, 0);

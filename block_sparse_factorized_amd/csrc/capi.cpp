@@ -47,7 +47,7 @@ int device_layout(sa_layout* L, int dev, DevLayout* out)
         *out = it->second;
         return SA_OK;
     }
-    const size_t nqb1 = (size_t)L->nqb + 1, nnz = (size_t)L->nnz;
+    const size_t nqb1 = (size_t)L->nqb + 1, nkb1 = (size_t)L->nkb + 1, nnz = (size_t)L->nnz;
     const size_t nwords = L->masks.size();
     // Sections, each 256-byte aligned: masks first (8-byte words).
     auto al = [](size_t x) { return (x + 255) & ~(size_t)255; };
@@ -61,7 +61,7 @@ int device_layout(sa_layout* L, int dev, DevLayout* out)
     size_t off_col_idx = al(off_row_ptr + nqb1 * 4);
     size_t off_mask_id = al(off_col_idx + nnz * 4);
     size_t off_col_ptr = al(off_mask_id + nnz * 4);
-    size_t off_row_idx = al(off_col_ptr + nqb1 * 4);
+    size_t off_row_idx = al(off_col_ptr + nkb1 * 4);
     size_t off_col_mask = al(off_row_idx + nnz * 4);
     const Groups* gs[2] = {&L->qgroups, &L->kgroups};
     size_t off_gptr[2], off_gblk[2], off_gstep[2];
@@ -126,7 +126,7 @@ int device_layout(sa_layout* L, int dev, DevLayout* out)
         for (size_t a = 0; a < nnz; ++a) col_mask[a] = L->mask_id[L->csr_pos[a]];
         memcpy(&host[off_col_mask], col_mask.data(), nnz * 4);
     }
-    memcpy(&host[off_col_ptr], L->col_ptr.data(), nqb1 * 4);
+    memcpy(&host[off_col_ptr], L->col_ptr.data(), nkb1 * 4);
     // Quadrant occupancy of every mask (block size 64): bit 2*rh + ch.
     std::vector<uint8_t> quad((size_t)L->n_masks, 0);
     if (L->T == 64)
@@ -196,6 +196,10 @@ int device_layout(sa_layout* L, int dev, DevLayout* out)
     v.kgrp_mode = (const int32_t*)(b + off_kmode);
     v.vl = (int32_t)L->view_l;
     v.vm = (int32_t)L->view_m;
+    v.kcl = L->key_cl;
+    v.kgl = L->key_gl;
+    v.koff = L->key_off;
+    v.km = (int32_t)L->key_m;
     L->dev_mem[dev] = mem;
     L->dev[dev] = v;
     *out = v;
@@ -272,9 +276,14 @@ int get_plan(ListKind kind, int dev, int32_t B, int32_t H, sa_layout* const* hl,
 bool aligned16(const void* p) { return ((uintptr_t)p & 15) == 0; }
 
 // Checks shared by sa_fwd and sa_bwd; fills the head table.
+// compact: walk compact views (the forward and dQ kernels); the dK/dV
+// kernel walks those layouts in their raster form, whose key blocks have
+// more and shorter query lists (the compact view's first key blocks are
+// listed by almost every query block, and a few long workgroups would set
+// the launch time).
 int common_checks(const char* fn, const sa_layout_t* const* head_layout, int32_t B, int32_t H, int64_t n,
-                  int32_t d, int dtype, float scale, bool backward, HeadTable* ht, std::vector<sa_layout*>* hl,
-                  sa_layout** distinct_out, int* n_distinct)
+                  int32_t d, int dtype, float scale, bool backward, bool compact, HeadTable* ht,
+                  std::vector<sa_layout*>* hl, sa_layout** distinct_out, int* n_distinct)
 {
     if (!head_layout) return fail(SA_ERR_INVALID_ARG, "%s: head_layout is NULL", fn);
     if (B < 1 || H < 1) return fail(SA_ERR_INVALID_ARG, "%s: B = %d, H = %d must be >= 1", fn, B, H);
@@ -304,7 +313,7 @@ int common_checks(const char* fn, const sa_layout_t* const* head_layout, int32_t
         if (L->T != block)
             return fail(SA_ERR_UNSUPPORTED, "%s: head_layout[%d] has block %d; %s kernels need block %d", fn, h, L->T,
                         dtype == SA_F32 ? "f32" : "bf16", block);
-        if (L->rview) L = L->rview;  // residue view: the kernels walk its dense causal layout
+        if (L->view && (compact || L->view_kind != 2)) L = L->view;  // the kernels walk the view
         int idx = -1;
         for (int a = 0; a < nl; ++a)
             if (distinct[a] == L) idx = a;
@@ -381,14 +390,20 @@ int sa_layout_export(const sa_layout_t* lay, int32_t* row_ptr, int32_t* col_idx,
     return SA_OK;
 }
 
+namespace {
+void drop_view(sa_layout_t* lay)
+{
+    if (lay->view) sa_layout_destroy(lay->view);
+    lay->view = nullptr;
+    lay->view_kind = 0;
+}
+}  // namespace
+
 int sa_layout_set_residue_view(sa_layout_t* lay, int enable)
 {
     if (!lay) return fail(SA_ERR_INVALID_ARG, "sa_layout_set_residue_view: layout is NULL");
     if (!enable) {
-        if (lay->rview) {
-            sa_layout_destroy(lay->rview);
-            lay->rview = nullptr;
-        }
+        if (lay->view_kind == 1) drop_view(lay);
         return SA_OK;
     }
     if (lay->pattern != SA_STRIDED_B)
@@ -398,21 +413,62 @@ int sa_layout_set_residue_view(sa_layout_t* lay, int enable)
     if (lay->n % lay->l != 0)
         return fail(SA_ERR_UNSUPPORTED, "sa_layout_set_residue_view: n = %lld is not a multiple of l = %lld",
                     (long long)lay->n, (long long)lay->l);
-    if (lay->rview) return SA_OK;
+    if (lay->view_kind == 1) return SA_OK;
     const int64_t m = lay->n / lay->l, m_pad = (m + 63) / 64 * 64;
     sa_layout* rv = nullptr;
     int st = build_layout(SA_DENSE_CAUSAL, m_pad, 1, 0, 64, &rv);
     if (st != SA_OK) return st;
     rv->view_l = lay->l;
     rv->view_m = m;
-    lay->rview = rv;
+    rv->key_m = m;
+    lay->view = rv;
+    lay->view_kind = 1;
+    return SA_OK;
+}
+
+int sa_layout_set_compact_view(sa_layout_t* lay, int enable)
+{
+    if (!lay) return fail(SA_ERR_INVALID_ARG, "sa_layout_set_compact_view: layout is NULL");
+    if (!enable) {
+        if (lay->view_kind == 2) drop_view(lay);
+        return SA_OK;
+    }
+    if (lay->pattern != SA_FIXED_B)
+        return fail(SA_ERR_UNSUPPORTED, "sa_layout_set_compact_view: only fixed B layouts have a compact view");
+    if (lay->T != 64)
+        return fail(SA_ERR_UNSUPPORTED, "sa_layout_set_compact_view: needs block 64 (the bf16 kernels)");
+    if (lay->n % lay->l != 0)
+        return fail(SA_ERR_UNSUPPORTED, "sa_layout_set_compact_view: n = %lld is not a multiple of l = %lld",
+                    (long long)lay->n, (long long)lay->l);
+    if ((lay->c & (lay->c - 1)) != 0)
+        return fail(SA_ERR_UNSUPPORTED, "sa_layout_set_compact_view: c = %lld is not a power of two",
+                    (long long)lay->c);
+    if (lay->view_kind == 2) return SA_OK;
+    sa_layout* cv = nullptr;
+    int st = build_compact_view(lay->n, lay->l, lay->c, &cv);
+    if (st != SA_OK) return st;
+    lay->view = cv;
+    lay->view_kind = 2;
+    return SA_OK;
+}
+
+int sa_layout_view_info(const sa_layout_t* lay, int* kind, int64_t* nqb, int64_t* nkb, int64_t* nnz,
+                        int64_t* allowed_pairs)
+{
+    if (!lay) return fail(SA_ERR_INVALID_ARG, "sa_layout_view_info: layout is NULL");
+    const sa_layout* v = lay->view ? lay->view : lay;
+    if (kind) *kind = lay->view_kind;
+    if (nqb) *nqb = v->nqb;
+    if (nkb) *nkb = v->nkb;
+    if (nnz) *nnz = v->nnz;
+    if (allowed_pairs) *allowed_pairs = v->allowed;
     return SA_OK;
 }
 
 void sa_layout_destroy(sa_layout_t* lay)
 {
     if (!lay) return;
-    if (lay->rview) sa_layout_destroy(lay->rview);
+    if (lay->view) sa_layout_destroy(lay->view);
     for (auto& kv : lay->dev_mem) {
         int cur = 0;
         if (hipGetDevice(&cur) == hipSuccess && hipSetDevice(kv.first) == hipSuccess) {
@@ -430,7 +486,7 @@ int sa_fwd(const sa_layout_t* const* head_layout, int32_t B, int32_t H, int64_t 
     int dev = 0, nl = 0;
     std::vector<sa_layout*> hl;
     sa_layout* distinct[kMaxLayouts];
-    int st = common_checks("sa_fwd", head_layout, B, H, n, d, dtype, scale, false, &ht, &hl, distinct, &nl);
+    int st = common_checks("sa_fwd", head_layout, B, H, n, d, dtype, scale, false, true, &ht, &hl, distinct, &nl);
     if (st != SA_OK) return st;
     if (!q || !k || !v || !o || !lse) return fail(SA_ERR_INVALID_ARG, "sa_fwd: NULL tensor pointer");
     if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || ((uintptr_t)lse & 3))
@@ -476,11 +532,14 @@ int bwd_call(const char* fn, int stages, const sa_layout_t* const* head_layout, 
              const float* lse, const void* dout, void* dq, void* dk, void* dv, void* workspace, size_t ws_bytes,
              void* stream)
 {
-    HeadTable ht;
-    int dev = 0, nl = 0;
-    std::vector<sa_layout*> hl;
+    HeadTable ht, htk;  // htk: for the dK/dV kernel (no compact views)
+    int dev = 0, nl = 0, nlk = 0;
+    std::vector<sa_layout*> hl, hlk;
     sa_layout* distinct[kMaxLayouts];
-    int st = common_checks(fn, head_layout, B, H, n, d, dtype, scale, true, &ht, &hl, distinct, &nl);
+    sa_layout* distinct_k[kMaxLayouts];
+    int st = common_checks(fn, head_layout, B, H, n, d, dtype, scale, true, true, &ht, &hl, distinct, &nl);
+    if (st != SA_OK) return st;
+    st = common_checks(fn, head_layout, B, H, n, d, dtype, scale, true, false, &htk, &hlk, distinct_k, &nlk);
     if (st != SA_OK) return st;
     // Pointers each stage reads or writes.
     const bool rt = stages & kStageRowTerms, kv = stages & kStageDkDv, dqs = stages & kStageDq;
@@ -500,9 +559,11 @@ int bwd_call(const char* fn, int stages, const sa_layout_t* const* head_layout, 
                     sa_bwd_workspace_size(B, H, n, d));
     st = prepare_device(distinct, nl, &ht, &dev);
     if (st != SA_OK) return st;
+    st = prepare_device(distinct_k, nlk, &htk, &dev);
+    if (st != SA_OK) return st;
     Plan pk{nullptr, 0}, pq{nullptr, 0};
     if (kv) {
-        st = get_plan(kByKeyPair, dev, B, H, hl.data(), &pk);
+        st = get_plan(kByKeyPair, dev, B, H, hlk.data(), &pk);
         if (st != SA_OK) return st;
     }
     if (dqs) {
@@ -536,11 +597,13 @@ int bwd_call(const char* fn, int stages, const sa_layout_t* const* head_layout, 
     }
     if (kv) {
         a.items = pk.items;
+        a.heads = htk;
         e = launch_bwd_dkdv_bf16_t64(d, a, pk.count, s);
         if (e != hipSuccess) return hip_fail(e, "sa_bwd: dK/dV kernel launch");
     }
     if (dqs) {
         a.items = pq.items;
+        a.heads = ht;
         e = launch_bwd_dq_bf16_t64(d, a, pq.count, s);
         if (e != hipSuccess) return hip_fail(e, "sa_bwd: dQ kernel launch");
     }

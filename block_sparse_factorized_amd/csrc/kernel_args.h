@@ -20,6 +20,13 @@ struct Item {
     int32_t pad;
 };
 
+// Sequence row of key t of a layout (DevLayout: key rows); t itself but in
+// the compact view of fixed B.
+__device__ inline int key_pos(const DevLayout& L, int t)
+{
+    return (t >> L.kcl) * L.kgl + L.koff + (t & ((1 << L.kcl) - 1));
+}
+
 struct HeadTable {
     DevLayout lay[kMaxLayouts];
     uint8_t head_lay[kMaxHeads];  // head -> index into lay

@@ -120,6 +120,32 @@ uint64_t next_serial()
     return ++s;
 }
 
+// From the listing by query block (row_ptr, col_idx, mask_id) and nkb: the
+// listing by key block and the two pair lists.
+void finish_layout(sa_layout* L)
+{
+    const int64_t nqb = L->nqb, nkb = L->nkb;
+    L->nnz = (int64_t)L->col_idx.size();
+    // Transpose: per key block, its query blocks in ascending order.
+    L->col_ptr.assign(nkb + 1, 0);
+    for (int32_t kb : L->col_idx) L->col_ptr[kb + 1]++;
+    for (int64_t kb = 0; kb < nkb; ++kb) L->col_ptr[kb + 1] += L->col_ptr[kb];
+    L->row_idx.assign(L->nnz, 0);
+    L->csr_pos.assign(L->nnz, 0);
+    std::vector<int32_t> fillp(L->col_ptr.begin(), L->col_ptr.end() - 1);
+    for (int64_t qb = 0; qb < nqb; ++qb)
+        for (int32_t a = L->row_ptr[qb]; a < L->row_ptr[qb + 1]; ++a) {
+            int32_t kb = L->col_idx[a];
+            int32_t slot = fillp[kb]++;
+            L->row_idx[slot] = (int32_t)qb;
+            L->csr_pos[slot] = a;
+        }
+    L->qgroups = pair_blocks(L->row_ptr, L->col_idx, L->mask_id);
+    std::vector<int32_t> col_mask(L->nnz);
+    for (int64_t a = 0; a < L->nnz; ++a) col_mask[a] = L->mask_id[L->csr_pos[a]];
+    L->kgroups = pair_blocks(L->col_ptr, L->row_idx, col_mask);
+}
+
 }  // namespace
 
 // Greedy pairing: each block, in ascending order, takes the unpaired block
@@ -206,6 +232,8 @@ int build_layout(int pattern, int64_t n, int64_t l, int64_t c, int32_t block, sa
         L->c = pattern == SA_FIXED_B ? c : 0;
         L->T = block;
         L->nqb = nqb;
+        L->nkb = nqb;
+        L->key_m = n;
         const Params p{pattern, l, L->c, block};
         const int64_t T = block, nw = T * T / 64;
 
@@ -241,31 +269,94 @@ int build_layout(int pattern, int64_t n, int64_t l, int64_t c, int32_t block, sa
             }
             L->row_ptr[qb + 1] = (int32_t)L->col_idx.size();
         }
-        L->nnz = (int64_t)L->col_idx.size();
         L->n_masks = (int64_t)ids.size();
         L->allowed = allowed;
-
-        // Transpose: per key block, its query blocks in ascending order.
-        L->col_ptr.assign(nqb + 1, 0);
-        for (int32_t kb : L->col_idx) L->col_ptr[kb + 1]++;
-        for (int64_t kb = 0; kb < nqb; ++kb) L->col_ptr[kb + 1] += L->col_ptr[kb];
-        L->row_idx.assign(L->nnz, 0);
-        L->csr_pos.assign(L->nnz, 0);
-        std::vector<int32_t> fillp(L->col_ptr.begin(), L->col_ptr.end() - 1);
-        for (int64_t qb = 0; qb < nqb; ++qb)
-            for (int32_t a = L->row_ptr[qb]; a < L->row_ptr[qb + 1]; ++a) {
-                int32_t kb = L->col_idx[a];
-                int32_t slot = fillp[kb]++;
-                L->row_idx[slot] = (int32_t)qb;
-                L->csr_pos[slot] = a;
-            }
-        L->qgroups = pair_blocks(L->row_ptr, L->col_idx, L->mask_id);
-        std::vector<int32_t> col_mask(L->nnz);
-        for (int64_t a = 0; a < L->nnz; ++a) col_mask[a] = L->mask_id[L->csr_pos[a]];
-        L->kgroups = pair_blocks(L->col_ptr, L->row_idx, col_mask);
+        finish_layout(L);
     } catch (const std::bad_alloc&) {
         delete L;
         return fail(SA_ERR_ALLOC, "sa_layout_build: out of host memory");
+    }
+    *out = L;
+    return SA_OK;
+}
+
+// Compact view of fixed B.  Fixed B lets query i see exactly the summary
+// positions (the last c of every l-block) at or before i ("OpenAI Sparse
+// Transformer", "Factorized Attention Patterns": a fixed set of columns;
+// pcnews.ru, "Разреженное внимание").  Numbered consecutively, the summary
+// positions are keys t = 0 .. (n/l) c - 1 at sequence row
+// (t / c) l + (l - c) + t mod c, increasing in t, so the keys query i sees
+// are a prefix: t < cnt(i), cnt(i) = floor((i+1)/l) c + max(0, (i+1) mod l
+// - (l - c)).  The view lists every query block against the 64-key blocks of
+// that prefix: a staircase of full blocks plus one partial block per query
+// block, the same allowed pairs as the fixed-B layout in about half as many
+// blocks of twice the density.
+int build_compact_view(int64_t n, int64_t l, int64_t c, sa_layout** out)
+{
+    *out = nullptr;
+    constexpr int64_t T = 64;
+    int kcl = 0;
+    while (((int64_t)1 << kcl) < c) ++kcl;
+    if (c < 1 || c > l || ((int64_t)1 << kcl) != c || n % l != 0 || n % T != 0)
+        return fail(SA_ERR_UNSUPPORTED, "compact view: needs n %% l == 0, n %% 64 == 0 and c a power of two <= l");
+    const int64_t nqb = n / T, nk = (n / l) * c, nkb = (nk + T - 1) / T;
+    if (l > ((int64_t)1 << 30) || nk > ((int64_t)1 << 30))
+        return fail(SA_ERR_UNSUPPORTED, "compact view: l or the key count does not fit 32 bits");
+    sa_layout* L = new (std::nothrow) sa_layout();
+    if (!L) return fail(SA_ERR_ALLOC, "compact view: out of host memory");
+    try {
+        L->serial = next_serial();
+        L->pattern = SA_FIXED_B;
+        L->n = n;
+        L->l = l;
+        L->c = c;
+        L->T = (int32_t)T;
+        L->nqb = nqb;
+        L->nkb = nkb;
+        L->view_l = 1;
+        L->view_m = n;
+        L->key_cl = kcl;
+        L->key_gl = (int32_t)l;
+        L->key_off = (int32_t)(l - c);
+        L->key_m = nk;
+        auto cnt = [&](int64_t i) { return (i + 1) / l * c + std::max<int64_t>(0, (i + 1) % l - (l - c)); };
+        std::unordered_map<std::vector<uint64_t>, int32_t, VecHash> ids;
+        std::vector<uint64_t> tile(T * T / 64);
+        L->row_ptr.assign(nqb + 1, 0);
+        int64_t allowed = 0;
+        for (int64_t qb = 0; qb < nqb; ++qb) {
+            const int64_t cmax = cnt(qb * T + T - 1);  // the widest row of the block
+            for (int64_t kb = 0; kb * T < cmax; ++kb) {
+                std::fill(tile.begin(), tile.end(), 0ull);
+                int64_t pop = 0;
+                for (int64_t r = 0; r < T; ++r) {
+                    const int64_t p = std::min<int64_t>(T, std::max<int64_t>(0, cnt(qb * T + r) - kb * T));
+                    if (p > 0) set_bits(tile.data(), r * T, r * T + p - 1);
+                    pop += p;
+                }
+                allowed += pop;
+                int32_t id = -1;
+                if (pop != T * T) {
+                    auto it = ids.find(tile);
+                    if (it == ids.end()) {
+                        id = (int32_t)ids.size();
+                        ids.emplace(tile, id);
+                        L->masks.insert(L->masks.end(), tile.begin(), tile.end());
+                    } else {
+                        id = it->second;
+                    }
+                }
+                L->col_idx.push_back((int32_t)kb);
+                L->mask_id.push_back(id);
+            }
+            L->row_ptr[qb + 1] = (int32_t)L->col_idx.size();
+        }
+        L->n_masks = (int64_t)ids.size();
+        L->allowed = allowed;
+        finish_layout(L);
+    } catch (const std::bad_alloc&) {
+        delete L;
+        return fail(SA_ERR_ALLOC, "compact view: out of host memory");
     }
     *out = L;
     return SA_OK;

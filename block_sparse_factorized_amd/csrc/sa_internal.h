@@ -33,7 +33,7 @@ struct DevLayout {
     //             4(L/32) + i%4, key 32w + L%32)       (lane = key column)
     const uint64_t* planes;
     const uint64_t* planes_t;
-    const int32_t* col_ptr;   // [nqb+1]   listing by key block
+    const int32_t* col_ptr;   // [nkb+1]   listing by key block
     const int32_t* row_idx;   // [nnz]     query blocks, ascending per key block
     const int32_t* col_mask;  // [nnz]     mask id of each transposed entry
     // Pairs of blocks with nearly the same list, walked together by one
@@ -62,6 +62,17 @@ struct DevLayout {
     // (stride l): vl = l, vm = n / l, walking a dense causal layout.
     int32_t vl;
     int32_t vm;
+    // Key rows.  Key t of the layout is sequence row key_pos(t) =
+    // (t >> kcl) * kgl + koff + (t & (2^kcl - 1)), and km keys are valid.
+    // Plain and residue views: kcl = 30, kgl = koff = 0 (key_pos(t) = t),
+    // km = vm.  The compact view of fixed B (c = 2^kcl summary columns at
+    // the end of every l = kgl positions): koff = l - c, km = (n / l) c, so
+    // the c summary keys of every l-block are consecutive keys.  Only the
+    // kernels that stream key tiles (forward, dQ) walk compact views.
+    int32_t kcl;
+    int32_t kgl;
+    int32_t koff;
+    int32_t km;
 };
 
 // Host-side pairing of one listing (see DevLayout).
@@ -80,7 +91,7 @@ struct sa_layout {
     int pattern;
     int64_t n, l, c;
     int32_t T;
-    int64_t nqb, nnz, n_masks, allowed;
+    int64_t nqb, nkb, nnz, n_masks, allowed;  // nkb: key blocks (nqb but in a compact view)
     std::vector<int32_t> row_ptr, col_idx, mask_id;
     std::vector<uint64_t> masks;
     std::vector<int32_t> col_ptr, row_idx, csr_pos;
@@ -89,10 +100,20 @@ struct sa_layout {
     // DevLayout): view_l = 1, view_m = n for a plain layout; the internal
     // dense causal layout behind a residue view has view_l = l, view_m = n/l.
     int64_t view_l = 1, view_m = 0;
-    // Residue view (strided B only): when set, the kernels run this layout's
-    // heads as l dense causal attentions over the residue classes mod l,
-    // walking `rview` (a dense causal layout on n/l rounded up to blocks).
-    sa_layout* rview = nullptr;
+    // Key rows of this layout when walked (see DevLayout): key_cl = 30,
+    // key_gl = key_off = 0, key_m = view_m unless this is a compact view.
+    int32_t key_cl = 30, key_gl = 0, key_off = 0;
+    int64_t key_m = 0;
+    // An alternate view the kernels walk instead of this layout, with the
+    // same results:
+    //  * residue view (strided B): the heads run as l dense causal attentions
+    //    over the residue classes mod l; `view` is a dense causal layout on
+    //    n/l rounded up to blocks, with view_l = l, view_m = n/l;
+    //  * compact view (fixed B): the keys are the c summary columns of every
+    //    l-block, consecutive; `view` lists query blocks against blocks of
+    //    those (n/l) c keys.
+    sa_layout* view = nullptr;
+    int view_kind = 0;  // 0 none, 1 residue, 2 compact
 
     std::mutex mu;                       // guards dev
     std::map<int, void*> dev_mem;        // device id -> allocation
@@ -103,6 +124,8 @@ namespace sa {
 
 // Layout builder (host only, layout.cpp).
 int build_layout(int pattern, int64_t n, int64_t l, int64_t c, int32_t block, sa_layout** out);
+// The compact view of fixed B (block 64; n % l == 0, c a power of two).
+int build_compact_view(int64_t n, int64_t l, int64_t c, sa_layout** out);
 
 // Error reporting (capi.cpp): records the message for sa_last_error and
 // returns `status`.

@@ -151,6 +151,40 @@ int sa_layout_export(const sa_layout_t* lay, int32_t* row_ptr, int32_t* col_idx,
  */
 int sa_layout_set_residue_view(sa_layout_t* lay, int enable);
 
+/*
+ * Compact view of a fixed-B layout ("OpenAI Sparse Transformer", "Factorized
+ * Attention Patterns", and pcnews.ru, "Разреженное внимание": fixed B lets a
+ * position attend a fixed set of summary columns, the last c of every block
+ * of l).  Numbered consecutively, the (n/l)·c summary positions are keys
+ * t = 0, 1, ... at sequence position (t / c)·l + (l - c) + t mod c, in
+ * increasing order, so the keys a query sees are a prefix of them.  With
+ * the view on, sa_fwd and the sa_bwd calls run this layout's heads against
+ * 64-key blocks of the summary keys (read in place, no copy): at n = 12288,
+ * l = 128, c = 32 that is 4656 blocks per head, almost all full, against the
+ * raster layout's 9216 half-empty ones.  The forward and the dQ stage walk
+ * the view; the dK/dV stage keeps walking the raster layout, whose key blocks
+ * have more and shorter query lists (in the view the first key blocks are
+ * listed by nearly every query block).  The results are those of the raster
+ * layout (same pairs; only the rounding order differs).  The layout itself (sa_layout_info,
+ * sa_layout_export) is unchanged.  enable = 0 turns the view off.
+ *
+ * Must not be called while an enqueued sa_fwd/sa_bwd uses the layout.
+ * Errors: SA_ERR_INVALID_ARG when lay == NULL; SA_ERR_UNSUPPORTED unless the
+ * pattern is SA_FIXED_B, the block is 64, n is a multiple of l and c is a
+ * power of two; SA_ERR_ALLOC when memory runs out.
+ */
+int sa_layout_set_compact_view(sa_layout_t* lay, int enable);
+
+/*
+ * What the kernels walk for this layout: *kind = 0 (the layout itself),
+ * 1 (residue view: a dense causal layout walked once per residue class,
+ * l times per head) or 2 (compact view), and that layout's query blocks,
+ * key blocks, listed blocks and allowed (query, key) pairs.  Any output
+ * pointer may be NULL.  Errors: SA_ERR_INVALID_ARG when lay == NULL.
+ */
+int sa_layout_view_info(const sa_layout_t* lay, int* kind, int64_t* nqb, int64_t* nkb, int64_t* nnz,
+                        int64_t* allowed_pairs);
+
 /* Free a layout and its device copies.  NULL is ignored.  The caller must
  * make sure no enqueued sa_fwd/sa_bwd still uses it. */
 void sa_layout_destroy(sa_layout_t* lay);

@@ -309,6 +309,85 @@ def test_residue_view_full_size_sampled(name):
         compare_head(x, res, b, h, pats[h], 1.0, True, fp32=False, rows=rows, kcols=kcols)
 
 
+# ---------------------------------------------------------------------------
+# Compact view of fixed B: the same pairs, walked over the summary keys only.
+
+COMPACT = [
+    # (head patterns, n, d, note); fixed B heads use the compact view
+    ([("fixed_b", 128, 32)], 1024, 64, "c = 32: two l-blocks per key block"),
+    ([("fixed_b", 128, 32)], 640, 64, "160 summary keys: ragged last key block"),
+    ([("fixed_b", 64, 8)], 768, 64, "c = 8: eight l-blocks per key block"),
+    ([("fixed_b", 256, 128)], 1024, 64, "c = 128: two key blocks per l-block"),
+    ([("fixed_b", 128, 128)], 512, 64, "c = l: no gaps (dense causal)"),
+    ([("fixed_b", 128, 32)], 1024, 128, "d = 128"),
+    ([("fixed_a", 128, 32), ("fixed_b", 128, 32), ("strided_b", 16, 1)], 1024, 64,
+     "raster, compact and residue-view heads in one call"),
+]
+
+
+def view_layouts(pats, n):
+    lays = layouts_for(pats, n, 64)
+    for (p, _, _), lay in zip(pats, lays):
+        if p == "fixed_b" and not lay.compact_view:
+            lay.set_compact_view(True)
+        if p == "strided_b" and not lay.residue_view:
+            lay.set_residue_view(True)
+    return lays
+
+
+@pytest.mark.parametrize("case", COMPACT, ids=[r[3] for r in COMPACT])
+def test_compact_view_matches_oracle(case):
+    pats, n, d, _ = case
+    H = len(pats)
+    x = workloads.custom_inputs((2, H, n, d), torch.bfloat16, seed=11 * n + d + H)
+    lays = view_layouts(pats, n)
+    assert any(lay.view_info()["kind"] == "compact" for lay in lays)
+    dev = {t: x[t].to(DEV) for t in ("q", "k", "v", "do")}
+    o, lse = sa.sa_fwd(dev["q"], dev["k"], dev["v"], lays, 1.0)
+    dq, dk, dv = sa.sa_bwd(dev["q"], dev["k"], dev["v"], o, lse, dev["do"], lays, 1.0)
+    torch.cuda.synchronize()
+    res = {"o": o.cpu(), "lse": lse.cpu(), "dq": dq.cpu(), "dk": dk.cpu(), "dv": dv.cpu()}
+    for b in range(2):
+        for h in range(H):
+            compare_head(x, res, b, h, pats[h], 1.0, True, fp32=False)
+
+
+def test_compact_view_every_output_written():
+    """NaN-filled outputs: the gaps between summary runs get exact zeros in
+    dK and dV, the empty first rows O = 0 and lse = -inf."""
+    pats, n, d = [("fixed_b", 128, 32), ("fixed_a", 128, 32)], 640, 64
+    x = workloads.custom_inputs((2, 2, n, d), torch.bfloat16, seed=98)
+    lays = view_layouts(pats, n)
+    q, k, v, do = (x[t].to(DEV) for t in ("q", "k", "v", "do"))
+    ref_o, ref_lse = sa.sa_fwd(q, k, v, lays, 1.0)
+    ref = sa.sa_bwd(q, k, v, ref_o, ref_lse, do, lays, 1.0)
+    nan = float("nan")
+    o = torch.full_like(q, nan)
+    lse = torch.full(q.shape[:3], nan, dtype=torch.float32, device=DEV)
+    sa.sa_fwd(q, k, v, lays, 1.0, o=o, lse=lse)
+    dq, dk, dv = (torch.full_like(q, nan) for _ in range(3))
+    sa.sa_bwd(q, k, v, o, lse, do, lays, 1.0, dq=dq, dk=dk, dv=dv)
+    torch.cuda.synchronize()
+    assert torch.equal(o, ref_o) and torch.equal(lse, ref_lse)
+    for got, want, nm in zip((dq, dk, dv), ref, ("dq", "dk", "dv")):
+        assert not torch.isnan(got.float()).any(), nm
+        assert torch.equal(got, want), nm
+    gap = (torch.arange(n, device=DEV) % 128) < 96  # non-summary positions of head 0
+    assert torch.count_nonzero(dk[:, 0][:, gap]) == 0 and torch.count_nonzero(dv[:, 0][:, gap]) == 0
+    assert torch.all(lse[:, 0, :96] == -math.inf) and torch.count_nonzero(o[:, 0, :96]) == 0
+
+
+def test_compact_view_full_size_sampled():
+    """The text workload at full size with its fixed-B heads in the compact view."""
+    w = WORKLOADS["text"]
+    x = workloads.make_inputs(w)
+    pats = w.head_patterns()
+    lays = view_layouts(pats, w.n)
+    res = run(x, pats, w.block, 1.0, backward=True, lays=lays)
+    for (b, h) in sample_heads(w.batch, w.heads):
+        compare_head(x, res, b, h, pats[h], 1.0, True, fp32=False)
+
+
 def test_autograd_wrapper_recomputes():
     """sparse_attention's gradients are sa_bwd's, bit for bit, and the only
     tensors it keeps besides q, k, v are O and lse (no n x n weights)."""

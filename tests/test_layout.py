@@ -220,3 +220,55 @@ def test_status_strings():
     for code in (sa.SA_OK, sa.SA_ERR_INVALID_ARG, sa.SA_ERR_UNSUPPORTED, sa.SA_ERR_HIP, sa.SA_ERR_ALLOC):
         assert lib.sa_status_string(code)
     assert lib.sa_status_string(-99) == b"unknown status"
+
+
+def test_compact_view_switch():
+    """The compact view is only for fixed B with block 64, l | n and c a power
+    of two; it leaves the layout's own listing unchanged, walks the same
+    allowed pairs, and can be switched off."""
+    lay = sa.sa_layout_build("fixed_b", 1024, 128, 32, block=64)
+    before = lay.export()
+    raster = lay.view_info()
+    assert raster["kind"] == "layout" and raster["nkb"] == raster["nqb"] == 16
+    lay.set_compact_view(True)
+    lay.set_compact_view(True)  # idempotent
+    after = lay.export()
+    for k in before:
+        assert np.array_equal(before[k], after[k]), k
+    v = lay.view_info()
+    assert v["kind"] == "compact" and v["allowed"] == lay.info()["allowed"]
+    assert v["nqb"] == 16 and v["nkb"] == 1024 // 128 * 32 // 64
+    lay.set_compact_view(False)
+    assert lay.view_info()["kind"] == "layout"
+    cases = [
+        (("fixed_a", 768, 128, 32, 64), sa.SA_ERR_UNSUPPORTED),
+        (("strided_b", 768, 8, 1, 64), sa.SA_ERR_UNSUPPORTED),
+        (("fixed_b", 768, 128, 32, 16), sa.SA_ERR_UNSUPPORTED),  # block 16: fp32 kernels
+        (("fixed_b", 768, 100, 32, 64), sa.SA_ERR_UNSUPPORTED),  # l does not divide n
+        (("fixed_b", 768, 128, 24, 64), sa.SA_ERR_UNSUPPORTED),  # c not a power of two
+    ]
+    for (p, n, l, c, T), code in cases:
+        bad = sa.sa_layout_build(p, n, l, c, block=T)
+        with pytest.raises(sa.SAError) as e:
+            bad.set_compact_view(True)
+        assert e.value.status == code
+        assert bad.view_info()["kind"] == "layout"
+
+
+@pytest.mark.parametrize("n,l,c", [(12288, 128, 32), (1024, 128, 32), (640, 128, 32), (768, 64, 8),
+                                   (1024, 256, 128), (1024, 128, 128), (4096, 256, 64), (2048, 64, 1)])
+def test_compact_view_blocks(n, l, c):
+    """The compact view walks exactly the fixed-B layout's allowed pairs, in
+    the number of 64 x 64 blocks the summary-key prefix predicts: query block
+    qb sees the first cnt(64 qb + 63) summary keys, cnt(i) = floor((i+1)/l) c
+    + max(0, (i+1) mod l - (l - c)), i.e. ceil(cnt / 64) key blocks.  At the
+    text workload's size that is 4656 blocks against the raster layout's 9216."""
+    lay = sa.sa_layout_build("fixed_b", n, l, c, block=64)
+    lay.set_compact_view(True)
+    v = lay.view_info()
+    assert v["allowed"] == lay.info()["allowed"]
+    cnt = lambda i: (i + 1) // l * c + max(0, (i + 1) % l - (l - c))
+    assert v["nnz"] == sum(-(-cnt(64 * qb + 63) // 64) for qb in range(n // 64))
+    assert v["nkb"] == -(-(n // l * c) // 64)
+    if (n, l, c) == (12288, 128, 32):
+        assert v["nnz"] == 4656 and lay.info()["nnz"] == 9216
