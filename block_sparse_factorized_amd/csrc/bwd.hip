@@ -217,14 +217,10 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(const BwdArgs a)
         st_nxt = ld_uniform(&L.kgrp_step[p0 + min(t + 2, nblk - 1)]);
         const int mid = member ? step.z : step.y;  // -2: this key block is not listed
         if (kb >= 0 && mid != -2) {
-            // Transposed lane-mask planes (set 0, all ones, for a full block),
-            // loaded before the products so the scalar loads overlap them.
+            // Transposed lane-mask planes (set 0, all ones, for a full block).
             // A 32-query half is live when the mask has an allowed element in
-            // quadrant (query half qt, key half wr).
+            // quadrant (query half qt, key half kh).
             const_u64* pl = (const_u64*)(L.planes_t + ((int64_t)(mid + 1) * 2 + kh) * 32);
-            uint64_t pln[32];
-#pragma unroll
-            for (int r = 0; r < 32; ++r) pln[r] = pl[r];
             const unsigned quad = (unsigned)step.w >> (4 * member);
             bool live[2];
 #pragma unroll
@@ -233,11 +229,16 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(const BwdArgs a)
             // One 32-query half at a time; a half with no allowed element for
             // this wave's keys is skipped entirely (it would only add zeros).
             // Masked elements get s = -inf, hence P = exp2(c2 s - lse log2 e)
-            // = 0 and dS = P (dP - D) = 0.
+            // = 0 and dS = P (dP - D) = 0.  The half is one straight-line
+            // block: its planes (scalar loads) and every LDS operand it needs
+            // are requested first, then the products, so the wave waits for
+            // memory once per half rather than once per product.
 #pragma unroll
             for (int qt = 0; qt < 2; ++qt)
                 if (live[qt]) {
-                    f32x16 s, dp;
+                    uint64_t pln[16];
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) pln[r] = pl[16 * qt + r];
                     bf16x8 qa[D / 16], oa[D / 16];
 #pragma unroll
                     for (int c = 0; c < D / 16; ++c) {
@@ -245,22 +246,14 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(const BwdArgs a)
                         oa[c] = *(const bf16x8*)(oc + aoff[c] + qt * 32 * TL::kRow);
                     }
                     // dP starts from -D of its query rows, so the product gives dP - D.
-                    zero(s);
+                    f32x16 s, dp;
+                    f32x4 nl[4];
 #pragma unroll
                     for (int g = 0; g < 4; ++g) {
                         const f32x4 nd = *(const f32x4*)&rc[T + 32 * qt + 8 * g + 4 * hh];
 #pragma unroll
                         for (int e = 0; e < 4; ++e) dp[4 * g + e] = nd[e];
-                    }
-#pragma unroll
-                    for (int c = 0; c < D / 16; ++c) {
-                        s = mfma(qa[c], kop[c], s);
-                        dp = mfma(oa[c], vop[c], dp);
-                    }
-                    if (mid >= 0) {
-#pragma unroll
-                        for (int i = 0; i < 16; ++i)
-                            s[i] = __builtin_amdgcn_inverse_ballot_w64(pln[16 * qt + i]) ? s[i] : -INFINITY;
+                        nl[g] = *(const f32x4*)&rc[32 * qt + 8 * g + 4 * hh];
                     }
                     bf16x8 ot[2][D / 32], qt8[2][D / 32];
 #pragma unroll
@@ -271,13 +264,24 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(const BwdArgs a)
                             ot[h][dt] = lds_read_tr8(oc + toff[0][dt] + cc * 16 * TL::kRow, oc + toff[1][dt] + cc * 16 * TL::kRow);
                             qt8[h][dt] = lds_read_tr8(qc + toff[0][dt] + cc * 16 * TL::kRow, qc + toff[1][dt] + cc * 16 * TL::kRow);
                         }
+                    zero(s);
+#pragma unroll
+                    for (int c = 0; c < D / 16; ++c) {
+                        s = mfma(qa[c], kop[c], s);
+                        dp = mfma(oa[c], vop[c], dp);
+                    }
+                    // all LDS reads first, then the S and dP products
+                    __builtin_amdgcn_sched_group_barrier(0x100, 2 * (D / 16) + 8 + 8 * (D / 32), 0);
+                    __builtin_amdgcn_sched_group_barrier(0x008, 2 * (D / 16), 0);
+#pragma unroll
+                    for (int i = 0; i < 16; ++i)
+                        s[i] = __builtin_amdgcn_inverse_ballot_w64(pln[i]) ? s[i] : -INFINITY;
 #pragma unroll
                     for (int g = 0; g < 4; ++g) {
-                        const f32x4 nl = *(const f32x4*)&rc[32 * qt + 8 * g + 4 * hh];
 #pragma unroll
                         for (int e = 0; e < 4; ++e) {
                             const int i = 4 * g + e;
-                            const float p = __builtin_amdgcn_exp2f(fmaf(s[i], c2, nl[e]));
+                            const float p = __builtin_amdgcn_exp2f(fmaf(s[i], c2, nl[g][e]));
                             s[i] = p;
                             dp[i] = p * dp[i];
                         }
