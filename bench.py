@@ -359,10 +359,11 @@ def main():
     ws = torch.empty(max(sa.sa_bwd_workspace_size(w.batch, w.heads, w.n, d), 16), dtype=torch.uint8, device=dev)
     scale = 1.0
 
-    # One step = forward + the three backward stages (the same kernels sa_bwd
-    # launches), each bracketed by events on torch's current stream -- the
-    # stream every launch goes to -- so every kernel is timed live.
-    names = ["fwd", "bwd_rowterms", "bwd_dkdv", "bwd_dq"] if w.backward else ["fwd"]
+    # One step = forward + the two backward stages (the same kernels sa_bwd
+    # launches: dQ with the row terms, then dK/dV), each bracketed by events
+    # on torch's current stream -- the stream every launch goes to -- so every
+    # kernel is timed live.
+    names = ["fwd", "bwd_dq", "bwd_dkdv"] if w.backward else ["fwd"]
 
     def step(ev=None):
         rec = (lambda i: ev[i].record()) if ev is not None else (lambda i: None)
@@ -370,12 +371,10 @@ def main():
         sa.sa_fwd(q, k, v, lays, scale, o=o, lse=lse)
         rec(1)
         if w.backward:
-            sa.sa_bwd_rowterms(o, lse, do, lays, scale, workspace=ws)
+            sa.sa_bwd_dq_rowterms(q, k, v, o, lse, do, lays, scale, workspace=ws, dq=dq)
             rec(2)
             sa.sa_bwd_dkdv(q, k, v, do, lays, scale, ws, dk=dk, dv=dv)
             rec(3)
-            sa.sa_bwd_dq(q, k, v, do, lays, scale, ws, dq=dq)
-            rec(4)
 
     for _ in range(args.warmup):
         step()
@@ -422,7 +421,7 @@ def main():
         "fwd": "fwd_bf16_t64_kernel<%d>" % d if w.dtype == "bf16" else "fwd_f32_t16_d64_kernel",
         "bwd_rowterms": "bwd_rowterms_kernel<%d>" % d,
         "bwd_dkdv": "bwd_dkdv_kernel<%d>" % d,
-        "bwd_dq": "bwd_dq_kernel<%d>" % d,
+        "bwd_dq": "bwd_dq_kernel<%d, true>" % d,
     }
     dk_ = kernels[dominant]
     kern_file = "fwd.hip" if dominant == "fwd" else "bwd.hip"

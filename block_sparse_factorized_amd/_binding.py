@@ -35,7 +35,8 @@ PATTERNS = {
 EXPORTED = [
     "sa_layout_build", "sa_layout_info", "sa_layout_export", "sa_layout_set_residue_view",
     "sa_layout_set_compact_view", "sa_layout_view_info", "sa_layout_destroy",
-    "sa_fwd", "sa_bwd", "sa_bwd_workspace_size", "sa_bwd_rowterms", "sa_bwd_dkdv", "sa_bwd_dq",
+    "sa_fwd", "sa_bwd", "sa_bwd_workspace_size", "sa_bwd_dq_rowterms", "sa_bwd_rowterms", "sa_bwd_dkdv",
+    "sa_bwd_dq",
     "sa_status_string", "sa_last_error",
 ]
 
@@ -77,6 +78,8 @@ def _load():
     lib.sa_bwd_rowterms.restype = cint
     lib.sa_bwd_dkdv.argtypes = [vp, i32, i32, i64, i32, cint, flt] + [vp] * 7 + [sz, vp]
     lib.sa_bwd_dkdv.restype = cint
+    lib.sa_bwd_dq_rowterms.argtypes = [vp, i32, i32, i64, i32, cint, flt] + [vp] * 8 + [sz, vp]
+    lib.sa_bwd_dq_rowterms.restype = cint
     lib.sa_bwd_dq.argtypes = [vp, i32, i32, i64, i32, cint, flt] + [vp] * 6 + [sz, vp]
     lib.sa_bwd_dq.restype = cint
     lib.sa_status_string.argtypes = [cint]
@@ -321,9 +324,25 @@ def _bwd_common(q, layouts, workspace):
     return B, H, n, d, _head_array(layouts, H), workspace
 
 
+def sa_bwd_dq_rowterms(q, k, v, o, lse, do, layouts, scale: float, workspace=None, dq=None, stream=None):
+    """First kernel of sa_bwd: dQ, and the row terms of every row into
+    ``workspace`` (allocated when None).  Returns (dq, workspace)."""
+    import torch
+    for name, t in (("k", k), ("v", v), ("o", o), ("do", do)):
+        _check_tensor(name, t, q.shape, q.dtype, q.device)
+    B, H, n, d, heads, workspace = _bwd_common(q, layouts, workspace)
+    _check_tensor("lse", lse, (B, H, n), torch.float32, q.device)
+    dq = torch.empty_like(q) if dq is None else dq
+    _check_tensor("dq", dq, q.shape, q.dtype, q.device)
+    _check(_lib.sa_bwd_dq_rowterms(heads, B, H, n, d, _dtype_code(q), float(scale), q.data_ptr(), k.data_ptr(),
+                                   v.data_ptr(), o.data_ptr(), lse.data_ptr(), do.data_ptr(), dq.data_ptr(),
+                                   workspace.data_ptr(), workspace.numel(), _stream_handle(stream, q.device)))
+    return dq, workspace
+
+
 def sa_bwd_rowterms(o, lse, do, layouts, scale: float, workspace=None, stream=None):
-    """Stage 1 of the backward: the row terms D_i = sum_t dO_it O_it and
-    -lse_i log2(e) into ``workspace`` (allocated and returned when None)."""
+    """The row terms alone: -D_i = -sum_t dO_it O_it and -lse_i log2(e)
+    into ``workspace`` (allocated and returned when None)."""
     import torch
     _check_tensor("do", do, o.shape, o.dtype, o.device)
     B, H, n, d, heads, workspace = _bwd_common(o, layouts, workspace)
@@ -335,7 +354,7 @@ def sa_bwd_rowterms(o, lse, do, layouts, scale: float, workspace=None, stream=No
 
 
 def sa_bwd_dkdv(q, k, v, do, layouts, scale: float, workspace, dk=None, dv=None, stream=None):
-    """Stage 2: dK, dV (needs the row terms in ``workspace``)."""
+    """dK, dV (needs the row terms in ``workspace``; sa_bwd's second kernel)."""
     import torch
     for name, t in (("k", k), ("v", v), ("do", do)):
         _check_tensor(name, t, q.shape, q.dtype, q.device)
@@ -351,7 +370,7 @@ def sa_bwd_dkdv(q, k, v, do, layouts, scale: float, workspace, dk=None, dv=None,
 
 
 def sa_bwd_dq(q, k, v, do, layouts, scale: float, workspace, dq=None, stream=None):
-    """Stage 3: dQ (needs the row terms in ``workspace``)."""
+    """dQ alone (needs the row terms in ``workspace``)."""
     import torch
     for name, t in (("k", k), ("v", v), ("do", do)):
         _check_tensor(name, t, q.shape, q.dtype, q.device)

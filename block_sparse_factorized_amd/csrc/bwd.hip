@@ -378,8 +378,10 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(const BwdArgs a)
 //   dP^T = V dO^T     C[key][q]  A = V rows (LDS)          B = dO^T (registers)
 //   dQ^T += K^T dS^T  C[d][q]    A = K^T (transposing LDS read)  B = dS^T
 // With d = 64 the kernel fits four waves per SIMD (its only spill is of a
-// value used after the loop).
-template <int D>
+// value used after the loop).  ROWTERMS: the kernel forms the row terms of
+// its rows from O, dO and lse itself and writes them to the workspace, so
+// that no row-term launch precedes it (the dK/dV kernel then runs after it).
+template <int D, bool ROWTERMS>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D == 64 ? 4 : 1))) void bwd_dq_kernel(
     const BwdArgs a)
 {
@@ -426,8 +428,33 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D == 64 ? 4
             dop[c] = *(const bf16x8*)(Or + 16 * c + 8 * hh);
         }
     }
-    const float nl2 = a.nl2[lrow0 + (uint32_t)(vl * q_rc)];
-    const float nd_i = a.ndelta[lrow0 + (uint32_t)(vl * q_rc)];
+    float nl2, nd_i;
+    const uint32_t trow = (uint32_t)(vl * q_rc);  // row-term index from lrow0
+    if constexpr (ROWTERMS) {
+        // The row terms of this wave's rows, as the row-term kernel forms
+        // them: -D_i = -sum_t dO_it O_it (lane hh holds d = 16c + 8hh .. +7,
+        // the other half comes from lane n + 32) and -lse_i log2(e).  They
+        // are written out for the dK/dV kernel, which runs after this one.
+        const unsigned short* Xr = (const unsigned short*)a.o + head + (uint32_t)(q_rc * rs);
+        float acc = 0.f;
+#pragma unroll
+        for (int c = 0; c < D / 16; ++c) {
+            const u32x4 x = *(const u32x4*)(Xr + 16 * c + 8 * hh);
+            const u32x4 y = __builtin_bit_cast(u32x4, dop[c]);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) acc += bf16_lo(x[e]) * bf16_lo(y[e]) + bf16_hi(x[e]) * bf16_hi(y[e]);
+        }
+        nd_i = -(acc + swap_halves(acc));
+        const float l = a.lse[lrow0 + trow];
+        nl2 = l == -INFINITY ? -INFINITY : -l * kLog2e;
+        if (hh == 0 && qb >= 0 && q_row < vm) {
+            a.ndelta[lrow0 + trow] = nd_i;
+            a.nl2[lrow0 + trow] = nl2;
+        }
+    } else {
+        nl2 = a.nl2[lrow0 + trow];
+        nd_i = a.ndelta[lrow0 + trow];
+    }
     // Byte offsets of the direct-to-LDS loads from the tile's first row (the
     // same for every tile but a ragged last one).
     uint32_t goff[NI];
@@ -593,12 +620,16 @@ hipError_t launch_bwd_dkdv_bf16_t64(int d, const BwdArgs& a, int n_items, hipStr
     return hipGetLastError();
 }
 
-hipError_t launch_bwd_dq_bf16_t64(int d, const BwdArgs& a, int n_items, hipStream_t stream)
+hipError_t launch_bwd_dq_bf16_t64(int d, const BwdArgs& a, int n_items, bool rowterms, hipStream_t stream)
 {
-    if (d == 64)
-        hipLaunchKernelGGL(bwd_dq_kernel<64>, dim3(n_items), dim3(256), 0, stream, a);
+    if (d == 64 && rowterms)
+        hipLaunchKernelGGL((bwd_dq_kernel<64, true>), dim3(n_items), dim3(256), 0, stream, a);
+    else if (d == 64)
+        hipLaunchKernelGGL((bwd_dq_kernel<64, false>), dim3(n_items), dim3(256), 0, stream, a);
+    else if (rowterms)
+        hipLaunchKernelGGL((bwd_dq_kernel<128, true>), dim3(n_items), dim3(256), 0, stream, a);
     else
-        hipLaunchKernelGGL(bwd_dq_kernel<128>, dim3(n_items), dim3(256), 0, stream, a);
+        hipLaunchKernelGGL((bwd_dq_kernel<128, false>), dim3(n_items), dim3(256), 0, stream, a);
     return hipGetLastError();
 }
 

@@ -525,7 +525,9 @@ size_t sa_bwd_workspace_size(int32_t B, int32_t H, int64_t n, int32_t d)
 
 namespace {
 
-enum BwdStage { kStageRowTerms = 1, kStageDkDv = 2, kStageDq = 4, kStageAll = 7 };
+// kStageDqRowTerms: the dQ kernel that also forms the row terms; it runs
+// first and the dK/dV kernel after it (sa_bwd).
+enum BwdStage { kStageRowTerms = 1, kStageDkDv = 2, kStageDq = 4, kStageDqRowTerms = 8 };
 
 int bwd_call(const char* fn, int stages, const sa_layout_t* const* head_layout, int32_t B, int32_t H, int64_t n,
              int32_t d, int dtype, float scale, const void* q, const void* k, const void* v, const void* o,
@@ -542,9 +544,10 @@ int bwd_call(const char* fn, int stages, const sa_layout_t* const* head_layout, 
     st = common_checks(fn, head_layout, B, H, n, d, dtype, scale, true, false, &htk, &hlk, distinct_k, &nlk);
     if (st != SA_OK) return st;
     // Pointers each stage reads or writes.
-    const bool rt = stages & kStageRowTerms, kv = stages & kStageDkDv, dqs = stages & kStageDq;
+    const bool rt = stages & kStageRowTerms, kv = stages & kStageDkDv, dqs = stages & (kStageDq | kStageDqRowTerms);
+    const bool dq_rt = stages & kStageDqRowTerms;
     std::vector<const void*> need = {workspace};
-    if (rt) need.insert(need.end(), {o, dout, (const void*)lse});
+    if (rt || dq_rt) need.insert(need.end(), {o, dout, (const void*)lse});
     if (kv || dqs) need.insert(need.end(), {q, k, v, dout});
     for (const void* p : need)
         if (!p) return fail(SA_ERR_INVALID_ARG, "%s: NULL pointer", fn);
@@ -591,6 +594,12 @@ int bwd_call(const char* fn, int stages, const sa_layout_t* const* head_layout, 
     a.items = nullptr;
     hipStream_t s = (hipStream_t)stream;
     hipError_t e;
+    if (dq_rt) {
+        a.items = pq.items;
+        a.heads = ht;
+        e = launch_bwd_dq_bf16_t64(d, a, pq.count, true, s);
+        if (e != hipSuccess) return hip_fail(e, "sa_bwd: dQ kernel launch");
+    }
     if (rt) {
         e = launch_bwd_rowterms_bf16(d, a, (int64_t)B * H * n, s);
         if (e != hipSuccess) return hip_fail(e, "sa_bwd: row-term kernel launch");
@@ -601,10 +610,10 @@ int bwd_call(const char* fn, int stages, const sa_layout_t* const* head_layout, 
         e = launch_bwd_dkdv_bf16_t64(d, a, pk.count, s);
         if (e != hipSuccess) return hip_fail(e, "sa_bwd: dK/dV kernel launch");
     }
-    if (dqs) {
+    if (dqs && !dq_rt) {
         a.items = pq.items;
         a.heads = ht;
-        e = launch_bwd_dq_bf16_t64(d, a, pq.count, s);
+        e = launch_bwd_dq_bf16_t64(d, a, pq.count, false, s);
         if (e != hipSuccess) return hip_fail(e, "sa_bwd: dQ kernel launch");
     }
     return SA_OK;
@@ -618,7 +627,7 @@ int sa_bwd(const sa_layout_t* const* head_layout, int32_t B, int32_t H, int64_t 
            const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dout, void* dq,
            void* dk, void* dv, void* workspace, size_t ws_bytes, void* stream)
 {
-    return bwd_call("sa_bwd", kStageAll, head_layout, B, H, n, d, dtype, scale, q, k, v, o, lse, dout, dq, dk, dv,
+    return bwd_call("sa_bwd", kStageDqRowTerms | kStageDkDv, head_layout, B, H, n, d, dtype, scale, q, k, v, o, lse, dout, dq, dk, dv,
                     workspace, ws_bytes, stream);
 }
 
@@ -636,6 +645,14 @@ int sa_bwd_dkdv(const sa_layout_t* const* head_layout, int32_t B, int32_t H, int
 {
     return bwd_call("sa_bwd_dkdv", kStageDkDv, head_layout, B, H, n, d, dtype, scale, q, k, v, nullptr, nullptr, dout,
                     nullptr, dk, dv, const_cast<void*>(workspace), ws_bytes, stream);
+}
+
+int sa_bwd_dq_rowterms(const sa_layout_t* const* head_layout, int32_t B, int32_t H, int64_t n, int32_t d, int dtype,
+                       float scale, const void* q, const void* k, const void* v, const void* o, const float* lse,
+                       const void* dout, void* dq, void* workspace, size_t ws_bytes, void* stream)
+{
+    return bwd_call("sa_bwd_dq_rowterms", kStageDqRowTerms, head_layout, B, H, n, d, dtype, scale, q, k, v, o, lse,
+                    dout, dq, nullptr, nullptr, workspace, ws_bytes, stream);
 }
 
 int sa_bwd_dq(const sa_layout_t* const* head_layout, int32_t B, int32_t H, int64_t n, int32_t d, int dtype,

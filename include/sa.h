@@ -215,7 +215,8 @@ size_t sa_bwd_workspace_size(int32_t B, int32_t H, int64_t n, int32_t d);
  * least sa_bwd_workspace_size(...) bytes, 16-byte aligned, owned by the
  * caller, contents ignored on entry.  Same errors as sa_fwd, plus
  * SA_ERR_INVALID_ARG when ws_bytes is too small.  Deterministic: no atomics,
- * so equal inputs give bitwise equal outputs.
+ * so equal inputs give bitwise equal outputs.  Runs sa_bwd_dq_rowterms then
+ * sa_bwd_dkdv (two kernels).
  */
 int sa_bwd(const sa_layout_t* const* head_layout, int32_t B, int32_t H, int64_t n, int32_t d,
            int dtype, float scale, const void* q, const void* k, const void* v, const void* o,
@@ -223,21 +224,28 @@ int sa_bwd(const sa_layout_t* const* head_layout, int32_t B, int32_t H, int64_t 
            size_t ws_bytes, void* stream);
 
 /*
- * The three stages of sa_bwd as separate calls, for callers that schedule
- * them themselves (for instance dQ and dK/dV on two streams once the row
- * terms are ready).  Arguments mean what they mean for sa_bwd; each call
- * reads and writes only the pointers it takes.
- *   sa_bwd_rowterms  the row terms -D_i = -sum_t dO_it O_it and -lse_i log2(e)
- *                    into the workspace
- *   sa_bwd_dkdv      dK, dV (reads the row terms from the workspace), one
- *                    workgroup per pair of key blocks walking their query
- *                    blocks
- *   sa_bwd_dq        dQ (reads the row terms from the workspace), one
- *                    workgroup per pair of query blocks walking their key
- *                    blocks
- * sa_bwd_dkdv and sa_bwd_dq must be ordered after sa_bwd_rowterms on the
- * device.  Same errors as sa_bwd.
+ * The stages of the backward pass as separate calls, for callers that
+ * schedule them themselves.  Arguments mean what they mean for sa_bwd; each
+ * call reads and writes only the pointers it takes.
+ *   sa_bwd_dq_rowterms  dQ, and the row terms -D_i = -sum_t dO_it O_it and
+ *                       -lse_i log2(e) of every row into the workspace, one
+ *                       workgroup per pair of query blocks walking their
+ *                       key blocks (sa_bwd's first kernel)
+ *   sa_bwd_dkdv         dK, dV (reads the row terms from the workspace), one
+ *                       workgroup per pair of key blocks walking their query
+ *                       blocks (sa_bwd's second kernel)
+ *   sa_bwd_rowterms     the row terms alone into the workspace
+ *   sa_bwd_dq           dQ (reads the row terms from the workspace)
+ * sa_bwd_dkdv and sa_bwd_dq must be ordered on the device after a call that
+ * wrote the row terms (sa_bwd_dq_rowterms or sa_bwd_rowterms).  The two
+ * routes give the same dQ, dK, dV up to the summation order of D_i (so not
+ * always bitwise); sa_bwd_dq_rowterms + sa_bwd_dkdv is bitwise sa_bwd.
+ * Same errors as sa_bwd.
  */
+int sa_bwd_dq_rowterms(const sa_layout_t* const* head_layout, int32_t B, int32_t H, int64_t n, int32_t d,
+                       int dtype, float scale, const void* q, const void* k, const void* v, const void* o,
+                       const float* lse, const void* dout, void* dq, void* workspace, size_t ws_bytes,
+                       void* stream);
 int sa_bwd_rowterms(const sa_layout_t* const* head_layout, int32_t B, int32_t H, int64_t n, int32_t d,
                     int dtype, float scale, const void* o, const float* lse, const void* dout,
                     void* workspace, size_t ws_bytes, void* stream);
