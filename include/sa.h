@@ -49,8 +49,10 @@
  * Otherwise they enqueue kernels on `stream` (a hipStream_t; NULL is the
  * default stream) and return SA_OK; device faults surface at the caller's
  * next synchronisation.  The first call with a new (B, H, layouts)
- * combination allocates and uploads a small work list (synchronously);
- * later calls reuse it.  Calls are thread-safe.
+ * combination allocates and uploads a small work list (synchronously), as
+ * does the first use of a layout on a device; later calls reuse them and
+ * only enqueue kernels, so they may be captured into a HIP graph (make one
+ * uncaptured call of each kind first).  Calls are thread-safe.
  *
  * Compiled (dtype, block, d) combinations:
  *     forward   (SA_F32, 16, 64), (SA_BF16, 64, 64), (SA_BF16, 64, 128)

@@ -426,6 +426,44 @@ def test_noncurrent_stream():
     assert torch.equal(o, ref_o)
 
 
+def test_graph_capture_replays():
+    """After one uncaptured call (which uploads the layouts and work lists),
+    sa_fwd + sa_bwd only enqueue kernels: captured into a graph and replayed
+    several times, with eager work between the replays, every replay gives
+    the eager results bit for bit."""
+    n = 1024
+    pats = [("strided_a", 128, 1), ("strided_b", 128, 1), ("fixed_a", 128, 32), ("fixed_b", 128, 32)]
+    x = workloads.custom_inputs((2, 4, n, 64), torch.bfloat16, seed=31)
+    lays = layouts_for(pats, n, 64)
+    q, k, v, do = (x[t].to(DEV) for t in ("q", "k", "v", "do"))
+    ref_o, ref_lse = sa.sa_fwd(q, k, v, lays, 1.0)
+    ref = sa.sa_bwd(q, k, v, ref_o, ref_lse, do, lays, 1.0)
+    o, lse = torch.empty_like(q), torch.empty(q.shape[:3], dtype=torch.float32, device=DEV)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(q), torch.empty_like(q)
+    ws = torch.empty(sa.sa_bwd_workspace_size(2, 4, n, 64), dtype=torch.uint8, device=DEV)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            sa.sa_fwd(q, k, v, lays, 1.0, o=o, lse=lse)
+            sa.sa_bwd(q, k, v, o, lse, do, lays, 1.0, dq=dq, dk=dk, dv=dv, workspace=ws)
+    torch.cuda.synchronize()
+    for rep in range(3):
+        for t in (o, dq, dk, dv):
+            t.fill_(float("nan"))
+        lse.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(o, ref_o) and torch.equal(lse, ref_lse), rep
+        for got, want, nm in zip((dq, dk, dv), ref, ("dq", "dk", "dv")):
+            assert torch.equal(got, want), (rep, nm)
+        sa.sa_fwd(q, k, v, lays, 1.0)  # eager work between replays
+        torch.cuda.synchronize()
+
+
 # ---------------------------------------------------------------------------
 # Workloads at full size, in the launch configuration the benchmark times.
 
