@@ -398,7 +398,7 @@ def main():
     # Counted (algorithmic) flops per launch, per listed block: forward 4*T*T*d;
     # backward 10*T*T*d split as dK/dV 8*T*T*d (S, dP, dV, dK) and dQ 2*T*T*d
     # (dQ itself; the S and dP it recomputes are not counted twice).
-    per_block = {"fwd": 4.0, "bwd_dkdv": 8.0, "bwd_dq": 2.0, "bwd_rowterms": 0.0}
+    per_block = {"fwd": 4.0, "bwd_dkdv": 8.0, "bwd_dq": 2.0}
     # Matrix-core flops the kernels execute, per live 32 x 32 quadrant
     # (forward S, PV; dK/dV S, dP, dV, dK; dQ S, dP, dQ).
     # The fp32 block-16 kernel skips nothing: it executes what is counted.
@@ -406,7 +406,7 @@ def main():
     quads = live_quadrants(lays, w.batch, T)
     quads_kv = live_quadrants(lays, w.batch, T, raster_compact=True) if args.compact_view else quads
     blocks_kv = sum(listed_blocks_dkdv(lay) for lay in lays) * w.batch
-    per_quad = {"fwd": 4.0, "bwd_dkdv": 8.0, "bwd_dq": 6.0, "bwd_rowterms": 0.0}
+    per_quad = {"fwd": 4.0, "bwd_dkdv": 8.0, "bwd_dq": 6.0}
     kernels = {}
     for nm in names:
         avg_s = float(kernel_ms[nm].mean()) * 1e-3
@@ -419,7 +419,6 @@ def main():
     dominant = max(names, key=lambda nm: kernels[nm]["avg_us"])
     kern_sym = {
         "fwd": "fwd_bf16_t64_kernel<%d>" % d if w.dtype == "bf16" else "fwd_f32_t16_d64_kernel",
-        "bwd_rowterms": "bwd_rowterms_kernel<%d>" % d,
         "bwd_dkdv": "bwd_dkdv_kernel<%d>" % d,
         "bwd_dq": "bwd_dq_kernel<%d, true>" % d,
     }

@@ -5,14 +5,15 @@
 // attention matrix is recomputed during backpropagation instead of stored.
 // Only O and lse come from the forward pass.  With c = scale:
 //     P_ij  = exp(c s_ij - lse_i)        (recomputed per block)
-//     D_i   = sum_t dO_it O_it           (row-term kernel)
+//     D_i   = sum_t dO_it O_it           (formed by the dQ kernel, or by
+//                                          the row-term kernel alone)
 //     dP_ij = dO_i . v_j,   dS_ij = P_ij (dP_ij - D_i)
-//     dV_j  = sum_i P_ij dO_i,  dK_j = c sum_i dS_ij q_i   (dK/dV kernel,
-//             one workgroup per pair of key blocks, walking their merged
-//             query-block lists)
 //     dQ_i  = c sum_j dS_ij k_j                             (dQ kernel, one
 //             workgroup per pair of query blocks, walking their merged
-//             key-block lists)
+//             key-block lists; runs first)
+//     dV_j  = sum_i P_ij dO_i,  dK_j = c sum_i dS_ij q_i   (dK/dV kernel,
+//             one workgroup per pair of key blocks, walking their merged
+//             query-block lists; runs second, reading the row terms)
 // Both kernels write their outputs once, with no atomics, so results are
 // deterministic.
 //
