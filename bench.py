@@ -85,6 +85,30 @@ def traffic_from_profile(kernel_file, kernel, workload):
     return None
 
 
+def measured_peaks():
+    """The machine's own denominators (libsa_peaks.so, include/sa_peaks.h):
+    the sustained bf16 MFMA rate of a kernel that does nothing else, and the
+    device-to-device copy bandwidth (bytes read + written per second)."""
+    import ctypes
+    import torch
+    path = os.path.join(ROOT, "block_sparse_factorized_amd", "_lib", "libsa_peaks.so")
+    lib = ctypes.CDLL(path)
+    lib.sap_mfma_bf16_tflops.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
+    lib.sap_mfma_bf16_tflops.restype = ctypes.c_double
+    lib.sap_copy_gbs.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int, ctypes.c_void_p]
+    lib.sap_copy_gbs.restype = ctypes.c_double
+    stream = torch.cuda.current_stream().cuda_stream
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    mfma = lib.sap_mfma_bf16_tflops(cus * 8, 2048, stream)
+    nbytes = 1 << 30
+    a = torch.empty(nbytes, dtype=torch.uint8, device="cuda:0")
+    b = torch.empty(nbytes, dtype=torch.uint8, device="cuda:0")
+    copy = lib.sap_copy_gbs(b.data_ptr(), a.data_ptr(), nbytes, 10, stream)
+    del a, b
+    return {"mfma_bf16_tflops": mfma if mfma > 0 else None, "hbm_copy_gbs": copy if copy > 0 else None,
+            "how": "bf16 32x32x16 MFMA loop (8 chains per wave), %d workgroups x 4 waves; 1 GiB device copy x 10" % (cus * 8)}
+
+
 def residue_blocks(lay):
     """(blocks per residue class, residue classes) of a residue view: a dense
     causal attention over n/l rows in blocks of 64."""
@@ -414,6 +438,8 @@ def main():
         fl = per_block[nm] * T * T * d * nb
         ex = per_quad[nm] * 32 * 32 * d * nq if T == 64 else fl
         kernels[nm] = {"avg_us": avg_s * 1e6, "median_us": float(np.median(kernel_ms[nm])) * 1e3,
+                       "p10_us": float(np.percentile(kernel_ms[nm], 10)) * 1e3,
+                       "p90_us": float(np.percentile(kernel_ms[nm], 90)) * 1e3,
                        "counted_gflop": fl / 1e9, "tflops": fl / avg_s / 1e12 if fl else None,
                        "executed_gflop": ex / 1e9, "executed_tflops": ex / avg_s / 1e12 if ex else None}
     dominant = max(names, key=lambda nm: kernels[nm]["avg_us"])
@@ -424,6 +450,11 @@ def main():
     }
     dk_ = kernels[dominant]
     kern_file = "fwd.hip" if dominant == "fwd" else "bwd.hip"
+    # The machine's own denominators, measured after the timed steps.
+    mp = measured_peaks() if w.dtype == "bf16" else None
+    mpeak = mp["mfma_bf16_tflops"] if mp else None
+    # Allowed (query, key) pairs over the elements of the walked blocks.
+    allowed = sum(lay.info()["allowed"] for lay in lays) * w.batch
     roofline = {
         "kernel": kern_sym[dominant],
         "bound": "mfma",
@@ -437,6 +468,7 @@ def main():
         # What the matrix cores actually execute (empty quadrants skipped).
         "executed_mfma_tflops": dk_["executed_tflops"],
         "executed_frac": dk_["executed_tflops"] / peak,
+        "frac_of_measured_peak": dk_["tflops"] / mpeak if mpeak else None,
     }
     out = {
         "metric": METRIC,
@@ -460,6 +492,9 @@ def main():
             "compact_view": bool(args.compact_view),
         },
         "frac_of_peak": value / peak,
+        "measured_peaks": mp,
+        "frac_of_measured_peak": value / mpeak if mpeak else None,
+        "useful_element_fraction": allowed / (blocks * T * T) if blocks else None,
         # With a residue or compact view, the raster layouts' block count over
         # the same step time (a reference only: the views walk fewer blocks).
         "raster_counted_tflops": (sum(lay.info()["nnz"] for lay in lays) * w.batch * 4.0 * T * T * d
@@ -468,6 +503,7 @@ def main():
         "live_quadrant_fraction": quads / (4.0 * blocks) if blocks else None,
         "kernels": kernels,
         "fwd_frac_of_peak": kernels["fwd"]["tflops"] / peak,
+        "fwd_frac_of_measured_peak": kernels["fwd"]["tflops"] / mpeak if mpeak else None,
         "layout_build_ms": layout_ms,
         "roofline": roofline,
         "cpu_baseline": None,

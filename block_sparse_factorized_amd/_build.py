@@ -15,6 +15,9 @@ OUT_DIR = os.path.join(HERE, "_lib")
 OBJ_DIR = os.path.join(HERE, "_build")
 LIB = os.path.join(OUT_DIR, "libsa.so")
 SOURCES = ["layout.cpp", "capi.cpp", "fwd.hip", "bwd.hip"]
+# libsa_peaks.so: the micro-benchmarks of include/sa_peaks.h (not part of libsa)
+PEAKS_LIB = os.path.join(OUT_DIR, "libsa_peaks.so")
+PEAKS_SOURCES = ["peaks.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 # -amdgpu-mfma-vgpr-form: keep MFMA accumulators in ordinary VGPRs, so the
@@ -34,21 +37,27 @@ def _compile(src: str) -> str:
     return obj
 
 
-def build(verbose: bool = False) -> str:
-    os.makedirs(OUT_DIR, exist_ok=True)
-    os.makedirs(OBJ_DIR, exist_ok=True)
-    with ThreadPoolExecutor(max_workers=min(4, len(SOURCES))) as ex:
-        objs = list(ex.map(_compile, SOURCES))
-    tmp = LIB + ".tmp%d" % os.getpid()
+def _link(objs, lib: str) -> None:
+    tmp = lib + ".tmp%d" % os.getpid()
     # --no-undefined: a kernel whose host stub failed to instantiate must
     # fail the build, not the first dlopen.
     cmd = [HIPCC, "--offload-arch=" + ARCH, "-shared", "-fPIC", "-Wl,--no-undefined", "-o", tmp] + objs
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError("link failed:\n%s\n%s" % (r.stdout, r.stderr))
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib)
+
+
+def build(verbose: bool = False) -> str:
+    os.makedirs(OUT_DIR, exist_ok=True)
+    os.makedirs(OBJ_DIR, exist_ok=True)
+    with ThreadPoolExecutor(max_workers=min(5, len(SOURCES) + len(PEAKS_SOURCES))) as ex:
+        objs = list(ex.map(_compile, SOURCES + PEAKS_SOURCES))
+    _link(objs[:len(SOURCES)], LIB)
+    _link(objs[len(SOURCES):], PEAKS_LIB)
     if verbose:
         print("built", LIB)
+        print("built", PEAKS_LIB)
     return LIB
 
 

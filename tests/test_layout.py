@@ -133,6 +133,17 @@ def test_header_symbols_exported():
     assert set(sa.EXPORTED) == names
 
 
+def test_peaks_header_symbols_exported():
+    """Every function include/sa_peaks.h declares is exported by libsa_peaks.so."""
+    text = open(os.path.join(ROOT, "include", "sa_peaks.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = set(re.findall(r"\b(sap_[a-z0-9_]+)\s*\(", text))
+    assert names == {"sap_mfma_bf16_tflops", "sap_copy_gbs"}
+    lib = ctypes.CDLL(os.path.join(os.path.dirname(sa.LIB_PATH), "libsa_peaks.so"))
+    for name in sorted(names):
+        assert hasattr(lib, name), name
+
+
 def _heads(*lays):
     return (ctypes.c_void_p * len(lays))(*[x.handle for x in lays])
 
