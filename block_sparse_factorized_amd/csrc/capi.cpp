@@ -215,10 +215,15 @@ enum ListKind { kByQuery = 0, kByQueryPair = 1, kByKeyPair = 2 };
 struct Plan {
     Item* items;
     int count;
+    int dev;
 };
 
 std::mutex g_plan_mu;
 std::map<std::string, Plan> g_plans;
+// layout serial -> keys of the cached work lists that name it; destroying the
+// layout frees them (sa_layout_destroy), so a process that keeps building and
+// destroying layouts does not accumulate work lists.
+std::map<uint64_t, std::vector<std::string>> g_plan_keys;
 
 int get_plan(ListKind kind, int dev, int32_t B, int32_t H, sa_layout* const* hl, Plan* out)
 {
@@ -267,10 +272,33 @@ int get_plan(ListKind kind, int dev, int32_t B, int32_t H, sa_layout* const* hl,
         (void)hipFree(mem);
         return hip_fail(e, "work list: hipMemcpy");
     }
-    Plan p{(Item*)mem, (int)count};
+    Plan p{(Item*)mem, (int)count, dev};
     g_plans[key] = p;
+    for (int32_t h = 0; h < H; ++h) {
+        std::vector<std::string>& keys = g_plan_keys[hl[h]->serial];
+        if (keys.empty() || keys.back() != key) keys.push_back(key);
+    }
     *out = p;
     return SA_OK;
+}
+
+// Frees the cached work lists that name layout `serial`.
+void release_plans(uint64_t serial)
+{
+    std::lock_guard<std::mutex> g(g_plan_mu);
+    auto it = g_plan_keys.find(serial);
+    if (it == g_plan_keys.end()) return;
+    for (const std::string& key : it->second) {
+        auto p = g_plans.find(key);
+        if (p == g_plans.end()) continue;
+        int cur = 0;
+        if (hipGetDevice(&cur) == hipSuccess && hipSetDevice(p->second.dev) == hipSuccess) {
+            (void)hipFree(p->second.items);
+            (void)hipSetDevice(cur);
+        }
+        g_plans.erase(p);
+    }
+    g_plan_keys.erase(it);
 }
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15) == 0; }
@@ -468,6 +496,7 @@ int sa_layout_view_info(const sa_layout_t* lay, int* kind, int64_t* nqb, int64_t
 void sa_layout_destroy(sa_layout_t* lay)
 {
     if (!lay) return;
+    release_plans(lay->serial);
     if (lay->view) sa_layout_destroy(lay->view);
     for (auto& kv : lay->dev_mem) {
         int cur = 0;

@@ -187,8 +187,9 @@ int sa_layout_set_compact_view(sa_layout_t* lay, int enable);
 int sa_layout_view_info(const sa_layout_t* lay, int* kind, int64_t* nqb, int64_t* nkb, int64_t* nnz,
                         int64_t* allowed_pairs);
 
-/* Free a layout and its device copies.  NULL is ignored.  The caller must
- * make sure no enqueued sa_fwd/sa_bwd still uses it. */
+/* Free a layout, its device copies and the cached work lists of every call
+ * that used it.  NULL is ignored.  The caller must make sure no enqueued
+ * sa_fwd/sa_bwd still uses it. */
 void sa_layout_destroy(sa_layout_t* lay);
 
 /*
