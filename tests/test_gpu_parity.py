@@ -426,6 +426,51 @@ def test_noncurrent_stream():
     assert torch.equal(o, ref_o)
 
 
+def _sweep_cases(count=32, seed=2019):
+    """Seeded random configurations: patterns mixed per head, n a multiple of
+    64 (some not a multiple of l), l and c anywhere in range, d 64 or 128,
+    batch and heads small, scale 1 or 1/sqrt(d), views switched on where
+    they apply."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for idx in range(count):
+        n = int(rng.choice([128, 192, 384, 512, 640, 896, 1024]))
+        H = int(rng.integers(1, 5))
+        B = int(rng.integers(1, 3))
+        d = int(rng.choice([64, 64, 128]))
+        pats = []
+        for _ in range(H):
+            p = str(rng.choice(["strided_a", "strided_b", "fixed_a", "fixed_b", "dense"]))
+            l = int(rng.choice([1, 3, 8, 16, 32, 64, 100, 128, 256, 2 * n]))
+            c = int(rng.integers(1, l + 1)) if p == "fixed_b" else 1
+            if p == "fixed_b" and rng.random() < 0.5:  # a power of two dividing l, for the compact view
+                c = 1 << int(rng.integers(0, max(1, int(np.log2(max(l, 1))) + 1)))
+                c = min(c, l)
+            pats.append((p, l, c))
+        scale = 1.0 if rng.random() < 0.5 else 1.0 / math.sqrt(d)
+        views = bool(rng.random() < 0.5)
+        out.append((idx, B, H, n, d, tuple(pats), scale, views))
+    return out
+
+
+@pytest.mark.parametrize("case", _sweep_cases(), ids=lambda c: "sweep%d" % c[0])
+def test_random_sweep_matches_oracle(case):
+    """Every output of a seeded random configuration against the oracle."""
+    idx, B, H, n, d, pats, scale, views = case
+    x = workloads.custom_inputs((B, H, n, d), torch.bfloat16, seed=500 + idx)
+    lays = layouts_for(list(pats), n, 64)
+    if views:
+        for (p, l, c), lay in zip(pats, lays):
+            if p == "strided_b" and n % l == 0 and not lay.residue_view:
+                lay.set_residue_view(True)
+            if p == "fixed_b" and n % l == 0 and (c & (c - 1)) == 0 and not lay.compact_view:
+                lay.set_compact_view(True)
+    res = run(x, list(pats), 64, scale, backward=True, lays=lays)
+    for b in range(B):
+        for h in range(H):
+            compare_head(x, res, b, h, pats[h], scale, True, fp32=False)
+
+
 def test_destroy_releases_work_lists():
     """Destroying a layout frees the cached work lists of the calls that used
     it: building, using and destroying fresh layouts over and over leaves the
