@@ -77,6 +77,28 @@ def test_layout_bit_exact_audio(pattern):
     check_against_oracle(pattern, 65536, 256, 1, 64)
 
 
+def _random_layout_cases(count=200, seed=1709):
+    """Seeded random (pattern, n, l, c, block): every block size, n a
+    multiple of the block (often not of l), l from 1 to beyond n, c anywhere
+    in 1..l."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for _ in range(count):
+        T = int(rng.choice([8, 16, 32, 64, 128]))
+        n = T * int(rng.integers(1, max(2, 1536 // T)))
+        p = str(rng.choice(["strided_a", "strided_b", "fixed_a", "fixed_b", "dense"]))
+        l = int(rng.integers(1, 2 * n + 2))
+        c = int(rng.integers(1, l + 1)) if p == "fixed_b" else 1
+        out.append((p, n, l, c, T))
+    return out
+
+
+@pytest.mark.parametrize("pattern,n,l,c,T", _random_layout_cases())
+def test_layout_bit_exact_random(pattern, n, l, c, T):
+    """Random layouts match the oracle's direct enumeration bit for bit."""
+    check_against_oracle(pattern, n, l, c, T)
+
+
 @pytest.mark.parametrize("pattern,n,l,c,T", SMALL[:10])
 def test_transpose_and_mask_ids(pattern, n, l, c, T):
     lay = sa.sa_layout_build(pattern, n, l, c, block=T)
