@@ -305,6 +305,42 @@ def test_bwd_against_autograd_of_bruteforce():
         np.testing.assert_allclose(dv, tv.grad.numpy(), rtol=1e-10, atol=1e-12)
 
 
+def _random_oracle_cases(count=30, seed=4242):
+    rng = np.random.default_rng(seed)
+    out = []
+    for _ in range(count):
+        p = str(rng.choice(["strided_a", "strided_b", "fixed_a", "fixed_b", "dense"]))
+        n = int(rng.integers(1, 97))
+        l = int(rng.integers(1, n + 9))
+        c = int(rng.integers(1, l + 1)) if p == "fixed_b" else 1
+        d = int(rng.integers(1, 9))
+        scale = float(rng.choice([0.25, 1.0, 2.0]))
+        out.append((p, n, l, c, d, scale))
+    return out
+
+
+@pytest.mark.parametrize("pattern,n,l,c,d,scale", _random_oracle_cases())
+def test_random_fwd_bwd_against_autograd_of_bruteforce(pattern, n, l, c, d, scale):
+    """Seeded random (pattern, n, l, c, d, scale): the oracle's O, lse and
+    gradients against the dense brute force and torch autograd through it
+    (fp64), including empty rows and l beyond n."""
+    seed = int(1000 * scale) + n * 7 + l * 13 + c + d
+    q, k, v, do = (rnd((n, d), seed + t) for t in range(4))
+    m = brute.mask(pattern, n, l, c)
+    o_ref, lse_ref, _ = brute.attention(q, k, v, m, scale)
+    tq, tk, tv = (torch.from_numpy(x).requires_grad_(True) for x in (q, k, v))
+    sc = (scale * tq @ tk.T).masked_fill(~torch.from_numpy(m), float("-inf"))
+    pr = torch.nan_to_num(torch.softmax(sc, dim=1), nan=0.0)
+    ((pr @ tv) * torch.from_numpy(do)).sum().backward()
+    dq, dk, dv, o, lse = oracle.head_bwd(pattern, l, c, q, k, v, do, scale)
+    np.testing.assert_allclose(o, o_ref, rtol=1e-11, atol=1e-12)
+    fin = np.isfinite(lse_ref)
+    assert np.array_equal(np.isfinite(lse), fin) and np.all(lse[~fin] == -np.inf)
+    np.testing.assert_allclose(lse[fin], lse_ref[fin], rtol=1e-11, atol=1e-12)
+    for got, want in ((dq, tq.grad), (dk, tk.grad), (dv, tv.grad)):
+        np.testing.assert_allclose(got, want.numpy(), rtol=1e-9, atol=1e-11)
+
+
 @pytest.mark.parametrize("pattern,n,l,c,T", [
     ("strided_a", 256, 16, 1, 16), ("strided_b", 256, 16, 1, 16), ("fixed_a", 512, 128, 32, 64),
     ("fixed_b", 512, 128, 32, 64), ("strided_b", 384, 40, 1, 32), ("fixed_b", 320, 20, 7, 16),
