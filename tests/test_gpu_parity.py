@@ -388,6 +388,23 @@ def test_compact_view_full_size_sampled():
         compare_head(x, res, b, h, pats[h], 1.0, True, fp32=False)
 
 
+def test_million_length_sampled():
+    """n = 2^20 with l = 1024 (the length-scaling run's largest point): a
+    strided-A head walked raster and a strided-B head in its residue view,
+    forward and backward, sampled rows and key columns against the oracle."""
+    n, d, l = 1 << 20, 64, 1024
+    pats = [("strided_a", l, 1), ("strided_b", l, 1)]
+    x = workloads.custom_inputs((1, 2, n, d), torch.bfloat16, seed=77)
+    lays = layouts_for(pats, n, 64)
+    lays[1].set_residue_view(True)
+    res = run(x, pats, 64, 1.0, backward=True, lays=lays)
+    rng = np.random.default_rng(1)
+    rows = np.unique(np.concatenate([np.arange(0, 16), rng.integers(0, n, 48), np.arange(n - 16, n)]))
+    kcols = np.unique(np.concatenate([np.arange(0, 8), rng.integers(0, n, 24), np.arange(n - 8, n)]))
+    for h in range(2):
+        compare_head(x, res, 0, h, pats[h], 1.0, True, fp32=False, rows=rows, kcols=kcols)
+
+
 def test_autograd_wrapper_recomputes():
     """sparse_attention's gradients are sa_bwd's, bit for bit, and the only
     tensors it keeps besides q, k, v are O and lse (no n x n weights)."""
