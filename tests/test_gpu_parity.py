@@ -182,6 +182,50 @@ def test_scales_and_sharp_logits(scale_kind):
         compare_head(x, res, 0, h, pats[h], scale, True, fp32=False)
 
 
+def _ramp_inputs(kind, n, d, seed):
+    """Q rows along one direction u and K rows placed along u by a per-key
+    ramp, so scores follow the ramp: "rising" puts every row's max at its
+    latest key (each block of the walk moves the running reference),
+    "falling" at its first, "spikes" at a few far-out keys of either sign.
+    Score differences reach about 700 (about 90 in scaled natural units)."""
+    rng = np.random.default_rng(seed)
+    u = rng.standard_normal(d)
+    u /= np.linalg.norm(u)
+    j = np.arange(n) / n
+    if kind == "rising":
+        ramp = 90.0 * j
+    elif kind == "falling":
+        ramp = 90.0 * (1.0 - j)
+    else:
+        ramp = rng.standard_normal(n) * 0.5
+        hit = rng.random(n) < 0.05
+        ramp[hit] = rng.choice([-1.0, 1.0], hit.sum()) * rng.uniform(20.0, 90.0, hit.sum())
+    q = 8.0 * u[None, :] + 0.1 * rng.standard_normal((n, d))
+    k = ramp[:, None] * u[None, :] + 0.1 * rng.standard_normal((n, d))
+    v = rng.standard_normal((n, d))
+    do = rng.standard_normal((n, d))
+    H = 4
+    t = lambda a: torch.from_numpy(np.broadcast_to(a, (1, H, n, d)).copy()).to(torch.bfloat16)
+    return {"q": t(q), "k": t(k), "v": t(v), "do": t(do)}
+
+
+@pytest.mark.parametrize("kind", ["rising", "falling", "spikes"])
+def test_running_reference_moves(kind):
+    """The forward's running reference: rows whose max keeps rising along the
+    walk, rows whose max comes first, and far-out spikes.  Forward only: on
+    these inputs dQ is a small difference of large terms, and rounding dS to
+    bf16 for the product alone moves it by 6-13 % (relative L2) from the
+    exact value, past the gradient bar, whatever the kernel does."""
+    n, d = 1024, 64
+    x = _ramp_inputs(kind, n, d, seed=5)
+    scale = 1.0 / math.sqrt(d)
+    pats = [("dense", 1, 1), ("strided_b", 128, 1), ("fixed_b", 128, 32), ("strided_a", 128, 1)]
+    res = run(x, pats, 64, scale, backward=False)
+    assert torch.isfinite(res["o"]).all()
+    for h in range(4):
+        compare_head(x, res, 0, h, pats[h], scale, False, fp32=False)
+
+
 def test_fp32_tiny_variants():
     for pats, n in (([("fixed_a", 32, 1), ("fixed_b", 32, 8)], 256), ([("strided_a", 20, 1), ("dense", 1, 1)], 160)):
         x = workloads.custom_inputs((2, 2, n, 64), torch.float32, seed=n, with_dout=False)
