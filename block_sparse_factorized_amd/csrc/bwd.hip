@@ -523,9 +523,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D == 64 ? 4
 #pragma unroll
             for (int r = 0; r < 32; ++r) pln[r] = pl[r];
             const unsigned quad = (unsigned)step.w >> (4 * member);
-            bool live[2];
+            bool live[2], partial[2];
 #pragma unroll
-            for (int kt = 0; kt < 2; ++kt) live[kt] = (quad >> (2 * wr + kt)) & 1u;
+            for (int kt = 0; kt < 2; ++kt) {
+                live[kt] = (quad >> (2 * wr + kt)) & 1u;
+                // (a half whose every element is allowed skips its lane masks)
+                partial[kt] = mid >= 0 && !((quad >> (8 + 2 * wr + kt)) & 1u);
+            }
 
             // One 32-key half at a time; a half with no allowed element for
             // this wave's rows is skipped entirely (it would only add zeros).
@@ -549,7 +553,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D == 64 ? 4
                         s = mfma(ka[c], qop[c], s);
                         dp = mfma(va[c], dop[c], dp);
                     }
-                    if (mid >= 0) {
+                    if (partial[kt]) {
 #pragma unroll
                         for (int i = 0; i < 16; ++i)
                             s[i] = __builtin_amdgcn_inverse_ballot_w64(pln[16 * kt + i]) ? s[i] : -INFINITY;

@@ -127,16 +127,26 @@ int device_layout(sa_layout* L, int dev, DevLayout* out)
         memcpy(&host[off_col_mask], col_mask.data(), nnz * 4);
     }
     memcpy(&host[off_col_ptr], L->col_ptr.data(), nkb1 * 4);
-    // Quadrant occupancy of every mask (block size 64): bit 2*rh + ch.
-    std::vector<uint8_t> quad((size_t)L->n_masks, 0);
+    // Quadrant occupancy of every mask (block size 64): bit 2*rh + ch of
+    // quad: quadrant (query half rh, key half ch) has an allowed element; of
+    // full: every element of it is allowed (its lane masks can be skipped).
+    std::vector<uint8_t> quad((size_t)L->n_masks, 0), full((size_t)L->n_masks, 0);
     if (L->T == 64)
-        for (int64_t m = 0; m < L->n_masks; ++m)
+        for (int64_t m = 0; m < L->n_masks; ++m) {
+            uint32_t all = 0xFu;
             for (int r = 0; r < 64; ++r) {
                 const uint64_t row = L->masks[m * 64 + r];  // query row r: bit s = key s
-                if (row & 0x00000000ffffffffull) quad[m] |= (uint8_t)(1u << (2 * (r / 32)));
-                if (row & 0xffffffff00000000ull) quad[m] |= (uint8_t)(1u << (2 * (r / 32) + 1));
+                const uint32_t lo = (uint32_t)row, hi = (uint32_t)(row >> 32);
+                const int rh = r / 32;
+                if (lo) quad[m] |= (uint8_t)(1u << (2 * rh));
+                if (hi) quad[m] |= (uint8_t)(1u << (2 * rh + 1));
+                if (lo != 0xffffffffu) all &= ~(1u << (2 * rh));
+                if (hi != 0xffffffffu) all &= ~(1u << (2 * rh + 1));
             }
+            full[m] = (uint8_t)all;
+        }
     auto quad_of = [&](int32_t m) -> uint32_t { return m == -1 ? 0xFu : m == -2 ? 0u : quad[m]; };
+    auto full_of = [&](int32_t m) -> uint32_t { return m == -1 ? 0xFu : m == -2 ? 0u : full[m]; };
     for (int k = 0; k < 2; ++k) {
         memcpy(&host[off_gptr[k]], gs[k]->ptr.data(), gs[k]->ptr.size() * 4);
         if (!gs[k]->blk.empty()) memcpy(&host[off_gblk[k]], gs[k]->blk.data(), gs[k]->blk.size() * 4);
@@ -145,7 +155,8 @@ int device_layout(sa_layout* L, int dev, DevLayout* out)
             st[x] = gs[k]->step[x];
             st[x + 1] = gs[k]->step[x + 1];
             st[x + 2] = gs[k]->step[x + 2];
-            st[x + 3] = (int32_t)(quad_of(st[x + 1]) | quad_of(st[x + 2]) << 4);
+            st[x + 3] = (int32_t)(quad_of(st[x + 1]) | quad_of(st[x + 2]) << 4 | full_of(st[x + 1]) << 8 |
+                                  full_of(st[x + 2]) << 12);
         }
     }
     // Key-block pairs: a member whose list only ever has allowed elements in

@@ -172,6 +172,9 @@ __global__ __launch_bounds__(256) void fwd_bf16_t64_kernel(const FwdArgs a)
             // weights: its scores, softmax and products are skipped, since they
             // would only add zeros to the output.  Bit kt of lv: half kt is live.
             const unsigned lv = ((unsigned)step.w >> (4 * member + 2 * wr)) & 3u;
+            // Bit kt of fl: every element of half kt is allowed, so its lane
+            // masks are not applied.
+            const unsigned fl = ((unsigned)step.w >> (8 + 4 * member + 2 * wr)) & 3u;
 
             // Each live half is folded in on its own: S^T = K Q^T, weights,
             // O^T += V^T P^T.  Register i of s holds key 32*kt + 8*(i/4) + 4*hh
@@ -181,12 +184,13 @@ __global__ __launch_bounds__(256) void fwd_bf16_t64_kernel(const FwdArgs a)
                 if ((lv >> kt) & 1u) {
                     f32x16 s;
                     // Operand reads, products, then the disallowed elements of
-                    // a partial block to -inf.
+                    // a partial half to -inf.
+                    const bool partial = mid >= 0 && !((fl >> kt) & 1u);
                     auto scores = [&]() {
                         // the half's 16 planes into SGPRs first, so the loads
                         // overlap the products
                         uint64_t pln[16];
-                        if (mid >= 0) {
+                        if (partial) {
 #pragma unroll
                             for (int r = 0; r < 16; ++r) pln[r] = pl[16 * kt + r];
                         }
@@ -198,7 +202,7 @@ __global__ __launch_bounds__(256) void fwd_bf16_t64_kernel(const FwdArgs a)
 #pragma unroll
                         for (int c = 0; c < D / 16; ++c)
                             s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop[c], qop[c], s, 0, 0, 0);
-                        if (mid >= 0) {
+                        if (partial) {
 #pragma unroll
                             for (int i = 0; i < 16; ++i)
                                 s[i] = __builtin_amdgcn_inverse_ballot_w64(pln[i]) ? s[i] : -INFINITY;

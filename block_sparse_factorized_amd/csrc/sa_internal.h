@@ -44,7 +44,8 @@ struct DevLayout {
     // block, -2 = that member does not list this block.  quadrants: bits 0-3
     // for a, 4-7 for b; bit 2*rh + ch is set when the member's mask has an
     // allowed element with query row in half rh and key in half ch of the
-    // 64 x 64 block (all four for a full block, none for -2).
+    // 64 x 64 block (all four for a full block, none for -2); bits 8-11 (a)
+    // and 12-15 (b) the same for quadrants whose every element is allowed.
     const int32_t* qgrp_ptr;
     const int2* qgrp_blk;
     const int4* qgrp_step;
