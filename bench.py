@@ -200,6 +200,7 @@ def cpu_baseline(w, x, pats, lays, T, max_heads):
     sample.sort(key=lambda bh: (bh[1] // 2, bh[0], bh[1] % 2))
     sample = sample[:max_heads]
     counted = 0.0
+    elements = 0
     t0 = time.perf_counter()
     for (b, h) in sample:
         p, l, c = pats[h]
@@ -210,6 +211,15 @@ def cpu_baseline(w, x, pats, lays, T, max_heads):
             oracle.head_fwd(p, l, c, *args[:3], 1.0)
         counted += listed_blocks(lays[h]) * 4.0 * T * T * w.d * (3.5 if w.backward else 1.0)
     secs = time.perf_counter() - t0
+    for (b, h) in sample:
+        p, l, c = pats[h]
+        elements += int(oracle.row_counts(p, w.n, l, c).sum())
+    cpu_model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            cpu_model = next((ln.split(":", 1)[1].strip() for ln in f if ln.startswith("model name")), None)
+    except OSError:
+        pass
     return {
         "value": counted / secs / 1e12,
         "unit": "TFLOP/s",
@@ -217,6 +227,10 @@ def cpu_baseline(w, x, pats, lays, T, max_heads):
         "kind": "oracle",
         "sample": "%d of %d heads of %s (b,h in A/B pairs), fwd%s in fp64, %.1f s"
                   % (len(sample), w.batch * w.heads, w.name, "+bwd" if w.backward else "", secs),
+        "seconds": secs,
+        "cpu_model": cpu_model,
+        # the oracle's own work: 4 d flops per allowed element forward, 10 d backward
+        "allowed_element_gflops": elements * w.d * (14.0 if w.backward else 4.0) / secs / 1e9,
     }
 
 
