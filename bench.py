@@ -469,6 +469,7 @@ def main():
     mpeak = mp["mfma_bf16_tflops"] if mp else None
     # Allowed (query, key) pairs over the elements of the walked blocks.
     allowed = sum(lay.info()["allowed"] for lay in lays) * w.batch
+    traffic = traffic_from_profile(kern_file, kern_sym[dominant], label)
     roofline = {
         "kernel": kern_sym[dominant],
         "bound": "mfma",
@@ -476,7 +477,9 @@ def main():
         "peak": peak,
         "unit": "TFLOP/s",
         "frac": dk_["tflops"] / peak,
-        "traffic": traffic_from_profile(kern_file, kern_sym[dominant], label),
+        "traffic": traffic,
+        # the counters' HBM bytes over this run's launch time
+        "achieved_hbm_gbs": traffic / (dk_["avg_us"] * 1e-6) / 1e9 if traffic else None,
         "counted_flops_per_launch": dk_["counted_gflop"] * 1e9,
         "avg_launch_us": dk_["avg_us"],
         # What the matrix cores actually execute (empty quadrants skipped).
