@@ -237,9 +237,13 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(const BwdArgs a)
 #pragma unroll
             for (int qt = 0; qt < 2; ++qt)
                 if (live[qt]) {
+                    // (a half whose every element is allowed skips its lane masks)
+                    const bool partial = ((quad >> (8 + 2 * qt + kh)) & 1u) == 0;
                     uint64_t pln[16];
+                    if (partial) {
 #pragma unroll
-                    for (int r = 0; r < 16; ++r) pln[r] = pl[16 * qt + r];
+                        for (int r = 0; r < 16; ++r) pln[r] = pl[16 * qt + r];
+                    }
                     bf16x8 qa[D / 16], oa[D / 16];
 #pragma unroll
                     for (int c = 0; c < D / 16; ++c) {
@@ -274,9 +278,11 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(const BwdArgs a)
                     // all LDS reads first, then the S and dP products
                     __builtin_amdgcn_sched_group_barrier(0x100, 2 * (D / 16) + 8 + 8 * (D / 32), 0);
                     __builtin_amdgcn_sched_group_barrier(0x008, 2 * (D / 16), 0);
+                    if (partial) {
 #pragma unroll
-                    for (int i = 0; i < 16; ++i)
-                        s[i] = __builtin_amdgcn_inverse_ballot_w64(pln[i]) ? s[i] : -INFINITY;
+                        for (int i = 0; i < 16; ++i)
+                            s[i] = __builtin_amdgcn_inverse_ballot_w64(pln[i]) ? s[i] : -INFINITY;
+                    }
 #pragma unroll
                     for (int g = 0; g < 4; ++g) {
 #pragma unroll
