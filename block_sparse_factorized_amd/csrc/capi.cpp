@@ -130,7 +130,7 @@ int device_layout(sa_layout* L, int dev, DevLayout* out)
     // Quadrant occupancy of every mask (block size 64): bit 2*rh + ch of
     // quad: quadrant (query half rh, key half ch) has an allowed element; of
     // full: every element of it is allowed (its lane masks can be skipped).
-    std::vector<uint8_t> quad((size_t)L->n_masks, 0), full((size_t)L->n_masks, 0);
+    std::vector<uint8_t> quad((size_t)L->n_masks, 0), full((size_t)L->n_masks, 0), one1((size_t)L->n_masks, 0);
     if (L->T == 64)
         for (int64_t m = 0; m < L->n_masks; ++m) {
             uint32_t all = 0xFu;
@@ -144,9 +144,25 @@ int device_layout(sa_layout* L, int dev, DevLayout* out)
                 if (hi != 0xffffffffu) all &= ~(1u << (2 * rh + 1));
             }
             full[m] = (uint8_t)all;
+            // one[m]: the forward's lane (hh, query r) holds keys 32*ch + 8*g + 4*hh + e
+            // (g, e < 4) of a quadrant; bit 2*rh + ch is set when every such
+            // lane has at most one allowed key there.
+            uint32_t one = 0xFu;
+            for (int r = 0; r < 64; ++r) {
+                const uint64_t row = L->masks[m * 64 + r];
+                for (int ch = 0; ch < 2; ++ch)
+                    for (int hh = 0; hh < 2; ++hh) {
+                        int cnt = 0;
+                        for (int g = 0; g < 4; ++g)
+                            for (int e = 0; e < 4; ++e) cnt += (int)((row >> (32 * ch + 8 * g + 4 * hh + e)) & 1ull);
+                        if (cnt > 1) one &= ~(1u << (2 * (r / 32) + ch));
+                    }
+            }
+            one1[m] = (uint8_t)(one & ~all);
         }
     auto quad_of = [&](int32_t m) -> uint32_t { return m == -1 ? 0xFu : m == -2 ? 0u : quad[m]; };
     auto full_of = [&](int32_t m) -> uint32_t { return m == -1 ? 0xFu : m == -2 ? 0u : full[m]; };
+    auto one_of = [&](int32_t m) -> uint32_t { return m < 0 ? 0u : one1[m]; };
     for (int k = 0; k < 2; ++k) {
         memcpy(&host[off_gptr[k]], gs[k]->ptr.data(), gs[k]->ptr.size() * 4);
         if (!gs[k]->blk.empty()) memcpy(&host[off_gblk[k]], gs[k]->blk.data(), gs[k]->blk.size() * 4);
@@ -156,7 +172,7 @@ int device_layout(sa_layout* L, int dev, DevLayout* out)
             st[x + 1] = gs[k]->step[x + 1];
             st[x + 2] = gs[k]->step[x + 2];
             st[x + 3] = (int32_t)(quad_of(st[x + 1]) | quad_of(st[x + 2]) << 4 | full_of(st[x + 1]) << 8 |
-                                  full_of(st[x + 2]) << 12);
+                                  full_of(st[x + 2]) << 12 | one_of(st[x + 1]) << 16 | one_of(st[x + 2]) << 20);
         }
     }
     // Key-block pairs: a member whose list only ever has allowed elements in

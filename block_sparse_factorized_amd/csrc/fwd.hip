@@ -175,6 +175,8 @@ __global__ __launch_bounds__(256) void fwd_bf16_t64_kernel(const FwdArgs a)
             // Bit kt of fl: every element of half kt is allowed, so its lane
             // masks are not applied.
             const unsigned fl = ((unsigned)step.w >> (8 + 4 * member + 2 * wr)) & 3u;
+            // Bit kt of o1: each lane has at most one allowed element in half kt.
+            const unsigned o1 = ((unsigned)step.w >> (16 + 4 * member + 2 * wr)) & 3u;
 
             // Each live half is folded in on its own: S^T = K Q^T, weights,
             // O^T += V^T P^T.  Register i of s holds key 32*kt + 8*(i/4) + 4*hh
@@ -183,17 +185,16 @@ __global__ __launch_bounds__(256) void fwd_bf16_t64_kernel(const FwdArgs a)
             for (int kt = 0; kt < 2; ++kt)
                 if ((lv >> kt) & 1u) {
                     f32x16 s;
-                    // Operand reads, products, then the disallowed elements of
-                    // a partial half to -inf.
                     const bool partial = mid >= 0 && !((fl >> kt) & 1u);
-                    auto scores = [&]() {
-                        // the half's 16 planes into SGPRs first, so the loads
-                        // overlap the products
-                        uint64_t pln[16];
-                        if (partial) {
+                    const bool one = (o1 >> kt) & 1u;  // (implies partial)
+                    // The half's 16 planes into SGPRs first, so the loads overlap
+                    // the products; then S^T = K Q^T.
+                    uint64_t pln[16];
+                    if (partial) {
 #pragma unroll
-                            for (int r = 0; r < 16; ++r) pln[r] = pl[16 * kt + r];
-                        }
+                        for (int r = 0; r < 16; ++r) pln[r] = pl[16 * kt + r];
+                    }
+                    {
                         bf16x8 kop[D / 16];
 #pragma unroll
                         for (int c = 0; c < D / 16; ++c) kop[c] = *(const bf16x8*)(kc + koff[c] + kt * 32 * TL::kRow);
@@ -202,12 +203,7 @@ __global__ __launch_bounds__(256) void fwd_bf16_t64_kernel(const FwdArgs a)
 #pragma unroll
                         for (int c = 0; c < D / 16; ++c)
                             s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop[c], qop[c], s, 0, 0, 0);
-                        if (partial) {
-#pragma unroll
-                            for (int i = 0; i < 16; ++i)
-                                s[i] = __builtin_amdgcn_inverse_ballot_w64(pln[i]) ? s[i] : -INFINITY;
-                        }
-                    };
+                    }
                     // Weights p = exp2(c2 s - mc), in place; returns this
                     // lane's sum of them.
                     auto weights = [&]() {
@@ -239,15 +235,28 @@ __global__ __launch_bounds__(256) void fwd_bf16_t64_kernel(const FwdArgs a)
                             for (int dt = 0; dt < D / 32; ++dt)
                                 oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop[h][dt], pb[h], oacc[dt], 0, 0, 0);
                     };
-                    scores();
-
                     // Lazy reference: the row max of the half is taken, but the
                     // reference m_ref (and with it the accumulator's scale) only
                     // moves when some weight against it would exceed 2^8, or when
-                    // the row had no reference yet.
-                    float mx = -INFINITY;
+                    // the row had no reference yet.  A half where each lane has at
+                    // most one allowed element (strided B's diagonal blocks) takes
+                    // that element's score x alone (-inf if the lane has none):
+                    // one exponential per lane instead of sixteen.  Otherwise the
+                    // disallowed elements of a partial half go to -inf first.
+                    float mx = -INFINITY, x = -INFINITY;
+                    if (one) {
 #pragma unroll
-                    for (int i = 0; i < 16; ++i) mx = __builtin_fmaxf(mx, s[i]);
+                        for (int i = 0; i < 16; ++i) x = __builtin_amdgcn_inverse_ballot_w64(pln[i]) ? s[i] : x;
+                        mx = x;
+                    } else {
+                        if (partial) {
+#pragma unroll
+                            for (int i = 0; i < 16; ++i)
+                                s[i] = __builtin_amdgcn_inverse_ballot_w64(pln[i]) ? s[i] : -INFINITY;
+                        }
+#pragma unroll
+                        for (int i = 0; i < 16; ++i) mx = __builtin_fmaxf(mx, s[i]);
+                    }
                     mx = half_max(mx);
                     const bool move = fmaf(mx, c2, -mc) > 8.f;
                     if (__builtin_amdgcn_ballot_w64(move)) {
@@ -263,7 +272,14 @@ __global__ __launch_bounds__(256) void fwd_bf16_t64_kernel(const FwdArgs a)
                             mc = mx * c2;
                         }
                     }
-                    l_run += weights();
+                    if (one) {
+                        const float p = __builtin_amdgcn_exp2f(fmaf(x, c2, -mc));
+                        l_run += p;
+#pragma unroll
+                        for (int i = 0; i < 16; ++i) s[i] = __builtin_amdgcn_inverse_ballot_w64(pln[i]) ? p : 0.f;
+                    } else {
+                        l_run += weights();
+                    }
                     products();
                 }
         }  // this wave's block lists the key block

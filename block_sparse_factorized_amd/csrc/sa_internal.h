@@ -45,7 +45,10 @@ struct DevLayout {
     // for a, 4-7 for b; bit 2*rh + ch is set when the member's mask has an
     // allowed element with query row in half rh and key in half ch of the
     // 64 x 64 block (all four for a full block, none for -2); bits 8-11 (a)
-    // and 12-15 (b) the same for quadrants whose every element is allowed.
+    // and 12-15 (b) the same for quadrants whose every element is allowed;
+    // bits 16-19 (a) and 20-23 (b) for partial quadrants where each lane of
+    // the forward's score layout holds at most one allowed element (a lane
+    // holds keys 32*ch + 8*g + 4*hh + e, g, e < 4, of one query).
     const int32_t* qgrp_ptr;
     const int2* qgrp_blk;
     const int4* qgrp_step;
