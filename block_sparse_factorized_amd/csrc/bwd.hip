@@ -384,11 +384,13 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(const BwdArgs a)
 //   S^T  = K Q^T      C[key][q]  A = K rows (LDS)          B = Q^T (registers)
 //   dP^T = V dO^T     C[key][q]  A = V rows (LDS)          B = dO^T (registers)
 //   dQ^T += K^T dS^T  C[d][q]    A = K^T (transposing LDS read)  B = dS^T
-// With d = 64 the kernel fits four waves per SIMD (its only spill is of a
-// value used after the loop).  ROWTERMS: the kernel forms the row terms of
-// its rows from O, dO and lse itself and writes them to the workspace, so
-// that no row-term launch precedes it (the dK/dV kernel then runs after it).
-template <int D, bool ROWTERMS>
+// With d = 64 the kernel fits four waves per SIMD (the ONE form spills one
+// value, used only after the loop).  ROWTERMS: the kernel forms the row
+// terms of its rows from O, dO and lse itself and writes them to the
+// workspace, so that no row-term launch precedes it (the dK/dV kernel then
+// runs after it).  ONE: quadrants whose lanes hold at most one allowed
+// element each take the one-exponential path.
+template <int D, bool ROWTERMS, bool ONE>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D == 64 ? 4 : 1))) void bwd_dq_kernel(
     const BwdArgs a)
 {
@@ -529,12 +531,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D == 64 ? 4
 #pragma unroll
             for (int r = 0; r < 32; ++r) pln[r] = pl[r];
             const unsigned quad = (unsigned)step.w >> (4 * member);
-            bool live[2], partial[2];
+            bool live[2], partial[2], one[2];
 #pragma unroll
             for (int kt = 0; kt < 2; ++kt) {
                 live[kt] = (quad >> (2 * wr + kt)) & 1u;
                 // (a half whose every element is allowed skips its lane masks)
                 partial[kt] = mid >= 0 && !((quad >> (8 + 2 * wr + kt)) & 1u);
+                // at most one allowed element per lane (used by the ONE form)
+                one[kt] = ONE && ((quad >> (16 + 2 * wr + kt)) & 1u);
             }
 
             // One 32-key half at a time; a half with no allowed element for
@@ -546,37 +550,71 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D == 64 ? 4
             for (int kt = 0; kt < 2; ++kt)
                 if (live[kt]) {
                     f32x16 s, dp;
-                    bf16x8 ka[D / 16], va[D / 16];
+                    bf16x8 kop[2][D / 32];
+                    // transposed K, the A operand of dQ^T += K^T dS^T
+                    auto read_kop = [&]() {
 #pragma unroll
-                    for (int c = 0; c < D / 16; ++c) {
-                        ka[c] = *(const bf16x8*)(kc + aoff[c] + kt * 32 * TL::kRow);
-                        va[c] = *(const bf16x8*)(vc + aoff[c] + kt * 32 * TL::kRow);
-                    }
+                        for (int h = 0; h < 2; ++h)
+#pragma unroll
+                            for (int dt = 0; dt < D / 32; ++dt) {
+                                const int cc = 2 * kt + h;
+                                kop[h][dt] = lds_read_tr8(kc + toff[0][dt] + cc * 16 * TL::kRow, kc + toff[1][dt] + cc * 16 * TL::kRow);
+                            }
+                    };
                     zero(s);
                     zero(dp);
+                    if constexpr (ONE) {
+                        // operands read per product (the registers the
+                        // one-element path needs)
 #pragma unroll
-                    for (int c = 0; c < D / 16; ++c) {
-                        s = mfma(ka[c], qop[c], s);
-                        dp = mfma(va[c], dop[c], dp);
-                    }
-                    if (partial[kt]) {
+                        for (int c = 0; c < D / 16; ++c) {
+                            const bf16x8 ka = *(const bf16x8*)(kc + aoff[c] + kt * 32 * TL::kRow);
+                            const bf16x8 va = *(const bf16x8*)(vc + aoff[c] + kt * 32 * TL::kRow);
+                            s = mfma(ka, qop[c], s);
+                            dp = mfma(va, dop[c], dp);
+                        }
+                    } else {
+                        bf16x8 ka[D / 16], va[D / 16];
 #pragma unroll
-                        for (int i = 0; i < 16; ++i)
-                            s[i] = __builtin_amdgcn_inverse_ballot_w64(pln[16 * kt + i]) ? s[i] : -INFINITY;
-                    }
-                    bf16x8 kop[2][D / 32];
-#pragma unroll
-                    for (int h = 0; h < 2; ++h)
-#pragma unroll
-                        for (int dt = 0; dt < D / 32; ++dt) {
-                            const int cc = 2 * kt + h;
-                            kop[h][dt] = lds_read_tr8(kc + toff[0][dt] + cc * 16 * TL::kRow, kc + toff[1][dt] + cc * 16 * TL::kRow);
+                        for (int c = 0; c < D / 16; ++c) {
+                            ka[c] = *(const bf16x8*)(kc + aoff[c] + kt * 32 * TL::kRow);
+                            va[c] = *(const bf16x8*)(vc + aoff[c] + kt * 32 * TL::kRow);
                         }
 #pragma unroll
-                    for (int i = 0; i < 16; ++i) {
-                        const float p = __builtin_amdgcn_exp2f(fmaf(s[i], c2, nl2));
-                        dp[i] = p * (dp[i] + nd_i);
+                        for (int c = 0; c < D / 16; ++c) {
+                            s = mfma(ka[c], qop[c], s);
+                            dp = mfma(va[c], dop[c], dp);
+                        }
                     }
+                    if (one[kt]) {
+                        // At most one allowed element per lane (strided B's
+                        // diagonal blocks): its P and dS alone, one
+                        // exponential instead of sixteen, then dS scattered
+                        // back (zero elsewhere).
+                        float x = -INFINITY, y = 0.f;
+#pragma unroll
+                        for (int i = 0; i < 16; ++i) {
+                            const bool b = __builtin_amdgcn_inverse_ballot_w64(pln[16 * kt + i]);
+                            x = b ? s[i] : x;
+                            y = b ? dp[i] : y;
+                        }
+                        const float ds = __builtin_amdgcn_exp2f(fmaf(x, c2, nl2)) * (y + nd_i);
+#pragma unroll
+                        for (int i = 0; i < 16; ++i) dp[i] = __builtin_amdgcn_inverse_ballot_w64(pln[16 * kt + i]) ? ds : 0.f;
+                    } else {
+                        if (partial[kt]) {
+#pragma unroll
+                            for (int i = 0; i < 16; ++i)
+                                s[i] = __builtin_amdgcn_inverse_ballot_w64(pln[16 * kt + i]) ? s[i] : -INFINITY;
+                        }
+                        if constexpr (!ONE) read_kop();
+#pragma unroll
+                        for (int i = 0; i < 16; ++i) {
+                            const float p = __builtin_amdgcn_exp2f(fmaf(s[i], c2, nl2));
+                            dp[i] = p * (dp[i] + nd_i);
+                        }
+                    }
+                    if constexpr (ONE) read_kop();
                     const bf16x8 db[2] = {pack8(dp, 0), pack8(dp, 8)};
 #pragma unroll
                     for (int h = 0; h < 2; ++h)
@@ -631,16 +669,21 @@ hipError_t launch_bwd_dkdv_bf16_t64(int d, const BwdArgs& a, int n_items, hipStr
     return hipGetLastError();
 }
 
-hipError_t launch_bwd_dq_bf16_t64(int d, const BwdArgs& a, int n_items, bool rowterms, hipStream_t stream)
+hipError_t launch_bwd_dq_bf16_t64(int d, const BwdArgs& a, int n_items, bool rowterms, bool one, hipStream_t stream)
 {
-    if (d == 64 && rowterms)
-        hipLaunchKernelGGL((bwd_dq_kernel<64, true>), dim3(n_items), dim3(256), 0, stream, a);
+    const dim3 g(n_items), b(256);
+    if (d == 64 && rowterms && one)
+        hipLaunchKernelGGL((bwd_dq_kernel<64, true, true>), g, b, 0, stream, a);
+    else if (d == 64 && rowterms)
+        hipLaunchKernelGGL((bwd_dq_kernel<64, true, false>), g, b, 0, stream, a);
     else if (d == 64)
-        hipLaunchKernelGGL((bwd_dq_kernel<64, false>), dim3(n_items), dim3(256), 0, stream, a);
+        hipLaunchKernelGGL((bwd_dq_kernel<64, false, false>), g, b, 0, stream, a);
+    else if (rowterms && one)
+        hipLaunchKernelGGL((bwd_dq_kernel<128, true, true>), g, b, 0, stream, a);
     else if (rowterms)
-        hipLaunchKernelGGL((bwd_dq_kernel<128, true>), dim3(n_items), dim3(256), 0, stream, a);
+        hipLaunchKernelGGL((bwd_dq_kernel<128, true, false>), g, b, 0, stream, a);
     else
-        hipLaunchKernelGGL((bwd_dq_kernel<128, false>), dim3(n_items), dim3(256), 0, stream, a);
+        hipLaunchKernelGGL((bwd_dq_kernel<128, false, false>), g, b, 0, stream, a);
     return hipGetLastError();
 }
 

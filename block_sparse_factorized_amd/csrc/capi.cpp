@@ -159,6 +159,7 @@ int device_layout(sa_layout* L, int dev, DevLayout* out)
                     }
             }
             one1[m] = (uint8_t)(one & ~all);
+            if (one1[m] & quad[m]) L->one_quads = true;
         }
     auto quad_of = [&](int32_t m) -> uint32_t { return m == -1 ? 0xFu : m == -2 ? 0u : quad[m]; };
     auto full_of = [&](int32_t m) -> uint32_t { return m == -1 ? 0xFu : m == -2 ? 0u : full[m]; };
@@ -650,10 +651,14 @@ int bwd_call(const char* fn, int stages, const sa_layout_t* const* head_layout, 
     a.items = nullptr;
     hipStream_t s = (hipStream_t)stream;
     hipError_t e;
+    // The dQ kernel's one-element form pays off where such quadrants occur
+    // (strided B); elsewhere the plain form keeps its grouped operand reads.
+    bool one = false;
+    for (int x = 0; x < nl; ++x) one = one || distinct[x]->one_quads;
     if (dq_rt) {
         a.items = pq.items;
         a.heads = ht;
-        e = launch_bwd_dq_bf16_t64(d, a, pq.count, true, s);
+        e = launch_bwd_dq_bf16_t64(d, a, pq.count, true, one, s);
         if (e != hipSuccess) return hip_fail(e, "sa_bwd: dQ kernel launch");
     }
     if (rt) {
@@ -669,7 +674,7 @@ int bwd_call(const char* fn, int stages, const sa_layout_t* const* head_layout, 
     if (dqs && !dq_rt) {
         a.items = pq.items;
         a.heads = ht;
-        e = launch_bwd_dq_bf16_t64(d, a, pq.count, false, s);
+        e = launch_bwd_dq_bf16_t64(d, a, pq.count, false, false, s);
         if (e != hipSuccess) return hip_fail(e, "sa_bwd: dQ kernel launch");
     }
     return SA_OK;

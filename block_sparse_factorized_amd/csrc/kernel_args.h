@@ -73,7 +73,10 @@ hipError_t launch_fwd_f32_t16(int d, const FwdArgs& a, int n_items, hipStream_t 
 hipError_t launch_bwd_rowterms_bf16(int d, const BwdArgs& a, int64_t rows, hipStream_t stream);
 hipError_t launch_bwd_dkdv_bf16_t64(int d, const BwdArgs& a, int n_items, hipStream_t stream);
 // rowterms: the dQ kernel also forms the row terms of its rows and writes
-// them to the workspace (no row-term launch before it).
-hipError_t launch_bwd_dq_bf16_t64(int d, const BwdArgs& a, int n_items, bool rowterms, hipStream_t stream);
+// them to the workspace (no row-term launch before it).  one (with
+// rowterms): the form with a one-exponential path for quadrants whose lanes
+// hold at most one allowed element each.
+hipError_t launch_bwd_dq_bf16_t64(int d, const BwdArgs& a, int n_items, bool rowterms, bool one,
+                                  hipStream_t stream);
 
 }  // namespace sa

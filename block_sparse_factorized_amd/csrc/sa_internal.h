@@ -118,6 +118,9 @@ struct sa_layout {
     //    those (n/l) c keys.
     sa_layout* view = nullptr;
     int view_kind = 0;  // 0 none, 1 residue, 2 compact
+    // Some partial quadrant leaves each lane of the forward's score layout
+    // at most one allowed element (set when the layout is first uploaded).
+    bool one_quads = false;
 
     std::mutex mu;                       // guards dev
     std::map<int, void*> dev_mem;        // device id -> allocation
