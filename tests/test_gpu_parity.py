@@ -226,6 +226,23 @@ def test_running_reference_moves(kind):
         compare_head(x, res, 0, h, pats[h], scale, False, fp32=False)
 
 
+@pytest.mark.parametrize("d", [64, 128])
+def test_one_element_quadrants(d):
+    """Layouts whose partial quadrants leave each lane of the forward's score
+    layout at most one allowed element (strided B at strides 32, 96 and 100,
+    fixed B with one summary column), which take the kernels'
+    one-exponential paths, beside fixed B with two summary columns (two in
+    one lane: the general path)."""
+    n = 1024
+    pats = [("strided_b", 32, 1), ("fixed_b", 64, 1), ("strided_b", 96, 1), ("fixed_b", 128, 2),
+            ("strided_b", 100, 1)]
+    x = workloads.custom_inputs((2, len(pats), n, d), torch.bfloat16, seed=40 + d)
+    res = run(x, pats, 64, 1.0 / math.sqrt(d), backward=True)
+    for b in range(2):
+        for h in range(len(pats)):
+            compare_head(x, res, b, h, pats[h], 1.0 / math.sqrt(d), True, fp32=False)
+
+
 def test_fp32_tiny_variants():
     for pats, n in (([("fixed_a", 32, 1), ("fixed_b", 32, 8)], 256), ([("strided_a", 20, 1), ("dense", 1, 1)], 160)):
         x = workloads.custom_inputs((2, 2, n, 64), torch.float32, seed=n, with_dout=False)
