@@ -460,7 +460,12 @@ def main():
     kern_sym = {
         "fwd": "fwd_bf16_t64_kernel<%d>" % d if w.dtype == "bf16" else "fwd_f32_t16_d64_kernel",
         "bwd_dkdv": "bwd_dkdv_kernel<%d>" % d,
-        "bwd_dq": "bwd_dq_kernel<%d, true>" % d,
+        # (the library launches the dQ kernel's one-element form when a walked
+        # layout has quadrants with at most one allowed element per lane:
+        # strided B walked raster, fixed B with one summary column)
+        "bwd_dq": "bwd_dq_kernel<%d, true, %s>" % (d, "true" if any(
+            (p == "strided_b" and not args.residue_view) or (p == "fixed_b" and c == 1)
+            for (p, l, c) in pats) else "false"),
     }
     dk_ = kernels[dominant]
     kern_file = "fwd.hip" if dominant == "fwd" else "bwd.hip"
