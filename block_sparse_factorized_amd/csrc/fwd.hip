@@ -31,9 +31,13 @@
 //   * Partial blocks are masked with 64-bit lane masks held in SGPRs (one
 //     v_cndmask per element).  A 32 x 32 quadrant of the block (this wave's
 //     32 rows, one 32-key half) with no allowed element is skipped: no score
-//     products, softmax or output products for it.
-//   * The running max is moved only when a row's max grows by more than
-//     2^8 in the exponent, so the accumulator rescale is rare.
+//     products, softmax or output products for it; one whose every element
+//     is allowed skips its masks; one where each lane holds at most one
+//     allowed element takes one exponential per lane.
+//   * Each live half is folded in on its own.  The running reference moves
+//     only when a weight against it would exceed 2^8 (the half's row max is
+//     more than 8 above it in log2 units), so the accumulator rescale is
+//     rare.
 //   * Work-list metadata is read with scalar loads, so waiting for it never
 //     waits for tiles in flight.
 //
