@@ -164,6 +164,7 @@ int device_layout(sa_layout* L, int dev, DevLayout* out)
     auto quad_of = [&](int32_t m) -> uint32_t { return m == -1 ? 0xFu : m == -2 ? 0u : quad[m]; };
     auto full_of = [&](int32_t m) -> uint32_t { return m == -1 ? 0xFu : m == -2 ? 0u : full[m]; };
     auto one_of = [&](int32_t m) -> uint32_t { return m < 0 ? 0u : one1[m]; };
+    int64_t pair_steps = 0, half_steps = 0;
     for (int k = 0; k < 2; ++k) {
         memcpy(&host[off_gptr[k]], gs[k]->ptr.data(), gs[k]->ptr.size() * 4);
         if (!gs[k]->blk.empty()) memcpy(&host[off_gblk[k]], gs[k]->blk.data(), gs[k]->blk.size() * 4);
@@ -174,8 +175,20 @@ int device_layout(sa_layout* L, int dev, DevLayout* out)
             st[x + 2] = gs[k]->step[x + 2];
             st[x + 3] = (int32_t)(quad_of(st[x + 1]) | quad_of(st[x + 2]) << 4 | full_of(st[x + 1]) << 8 |
                                   full_of(st[x + 2]) << 12 | one_of(st[x + 1]) << 16 | one_of(st[x + 2]) << 20);
+            if (k == 0)
+                for (int m = 0; m < 2; ++m)
+                    for (int wr = 0; wr < 2; ++wr) {
+                        const uint32_t lv = (quad_of(st[x + 1 + m]) >> (2 * wr)) & 3u;
+                        const uint32_t o1 = (one_of(st[x + 1 + m]) >> (2 * wr)) & 3u;
+                        if (lv == 3u && o1 != 3u)
+                            ++pair_steps;
+                        else if (lv != 0u)
+                            ++half_steps;
+                    }
         }
     }
+    L->fwd_pair_steps = pair_steps;
+    L->fwd_half_steps = half_steps;
     // Key-block pairs: a member whose list only ever has allowed elements in
     // one 32-key half gets mode 1 + that half (its two waves then share the
     // half and split the query halves), else mode 0.  Bits 0-1: member a,
@@ -565,8 +578,16 @@ int sa_fwd(const sa_layout_t* const* head_layout, int32_t B, int32_t H, int64_t 
     a.scale_log2 = scale * 1.4426950408889634f;
     a.items = plan.items;
     a.heads = ht;
-    hipError_t e = dtype == SA_BF16 ? launch_fwd_bf16_t64(d, a, plan.count, (hipStream_t)stream)
-                                    : launch_fwd_f32_t16(d, a, plan.count, (hipStream_t)stream);
+    // The paired form when most of the walk's wave-steps have both halves
+    // live (full blocks: dense layouts, residue views, wide strided A).
+    int64_t pair_steps = 0, half_steps = 0;
+    for (int32_t h = 0; h < H; ++h) {
+        pair_steps += hl[h]->fwd_pair_steps;
+        half_steps += hl[h]->fwd_half_steps;
+    }
+    hipError_t e = dtype == SA_BF16
+                       ? launch_fwd_bf16_t64(d, a, plan.count, pair_steps > half_steps, (hipStream_t)stream)
+                       : launch_fwd_f32_t16(d, a, plan.count, (hipStream_t)stream);
     if (e != hipSuccess) return hip_fail(e, "sa_fwd: kernel launch");
     return SA_OK;
 }

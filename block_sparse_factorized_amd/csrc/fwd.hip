@@ -51,7 +51,11 @@
 namespace sa {
 namespace {
 
-template <int D>
+// PAIRED: a step's two live halves are scored together and checked once (the
+// better form when most steps have both halves live: full blocks); else each
+// live half is folded in on its own (steps with one live half, or one
+// allowed element per lane).
+template <int D, bool PAIRED>
 __global__ __launch_bounds__(256) void fwd_bf16_t64_kernel(const FwdArgs a)
 {
     constexpr int T = 64;
@@ -125,10 +129,13 @@ __global__ __launch_bounds__(256) void fwd_bf16_t64_kernel(const FwdArgs a)
 #pragma unroll
         for (int i = 0; i < 16; ++i) oacc[dt][i] = 0.f;
     // Running reference m_ref (at most 8 / c2 below the row max seen so
-    // far), mc = m_ref * c2, running sum l_run.  While a row has no allowed
-    // key yet, m_ref = -inf and mc = -3e38: its first finite score then
-    // moves the reference, and its weights of -inf scores stay 0.
-    float m_ref = -INFINITY, mc = -3.0e38f, l_run = 0.f;
+    // far), mc = m_ref * c2, running sum l_run.  Per-half form: while a row
+    // has no allowed key yet, m_ref = -inf and mc = -3e38, so its first
+    // finite score moves the reference and its weights of -inf scores stay
+    // 0.  PAIRED form: mc = 0 while m_ref = -inf, and no_ref tells that some
+    // row of the wave has no reference yet.
+    float m_ref = -INFINITY, mc = PAIRED ? 0.f : -3.0e38f, l_run = 0.f;
+    bool no_ref = true;
     const float c2 = a.scale_log2;
 
     auto issue = [&](int kb, unsigned char* kd, unsigned char* vd) {
@@ -182,47 +189,104 @@ __global__ __launch_bounds__(256) void fwd_bf16_t64_kernel(const FwdArgs a)
             // Bit kt of o1: each lane has at most one allowed element in half kt.
             const unsigned o1 = ((unsigned)step.w >> (16 + 4 * member + 2 * wr)) & 3u;
 
-            // Each live half is folded in on its own: S^T = K Q^T, weights,
-            // O^T += V^T P^T.  Register i of s holds key 32*kt + 8*(i/4) + 4*hh
-            // + i%4 of query n.
+            if constexpr (PAIRED) {
+                // Both halves of the step together: their score products
+                // back to back, then one lazy check over the step.
+
+                // S^T = K Q^T: register i of s[kt] holds key 32*kt + 8*(i/4) + 4*hh + i%4 of query n.
+                // A live half's operand reads first, then its products; then the
+                // disallowed elements of a partial block to -inf.
+                f32x16 s[2];
+                auto scores = [&]() {
 #pragma unroll
-            for (int kt = 0; kt < 2; ++kt)
-                if ((lv >> kt) & 1u) {
-                    f32x16 s;
-                    const bool partial = mid >= 0 && !((fl >> kt) & 1u);
-                    const bool one = (o1 >> kt) & 1u;  // (implies partial)
-                    // The half's 16 planes into SGPRs first, so the loads overlap
-                    // the products; then S^T = K Q^T.
-                    uint64_t pln[16];
-                    if (partial) {
+                    for (int kt = 0; kt < 2; ++kt)
+                        if ((lv >> kt) & 1u) {
+                            // this half's 16 planes into SGPRs first, so the loads
+                            // overlap the products
+                            uint64_t pln[16];
+                            const bool partial = mid >= 0 && !((fl >> kt) & 1u);
+                            if (partial) {
 #pragma unroll
-                        for (int r = 0; r < 16; ++r) pln[r] = pl[16 * kt + r];
-                    }
-                    {
-                        bf16x8 kop[D / 16];
+                                for (int r = 0; r < 16; ++r) pln[r] = pl[16 * kt + r];
+                            }
+                            bf16x8 kop[D / 16];
 #pragma unroll
-                        for (int c = 0; c < D / 16; ++c) kop[c] = *(const bf16x8*)(kc + koff[c] + kt * 32 * TL::kRow);
+                            for (int c = 0; c < D / 16; ++c) kop[c] = *(const bf16x8*)(kc + koff[c] + kt * 32 * TL::kRow);
 #pragma unroll
-                        for (int i = 0; i < 16; ++i) s[i] = 0.f;
+                            for (int i = 0; i < 16; ++i) s[kt][i] = 0.f;
 #pragma unroll
-                        for (int c = 0; c < D / 16; ++c)
-                            s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop[c], qop[c], s, 0, 0, 0);
-                    }
-                    // Weights p = exp2(c2 s - mc), in place; returns this
-                    // lane's sum of them.
-                    auto weights = [&]() {
-                        float lsum = 0.f;
+                            for (int c = 0; c < D / 16; ++c)
+                                s[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop[c], qop[c], s[kt], 0, 0, 0);
+                            if (partial) {
 #pragma unroll
-                        for (int i = 0; i < 16; ++i) {
-                            const float p = __builtin_amdgcn_exp2f(fmaf(s[i], c2, -mc));
-                            s[i] = p;
-                            lsum += p;
+                                for (int i = 0; i < 16; ++i)
+                                    s[kt][i] = __builtin_amdgcn_inverse_ballot_w64(pln[i]) ? s[kt][i] : -INFINITY;
+                            }
                         }
-                        return lsum;
-                    };
-                    // O^T += V^T P^T (chunk h of this half's P^T is registers
-                    // 8h..8h+7 of s).
-                    auto products = [&]() {
+                };
+                // Weights p = exp2(c2 s - mc) of the live halves, in place; returns
+                // this lane's sum of them.
+                auto weights = [&]() {
+                    float lsum = 0.f;
+#pragma unroll
+                    for (int kt = 0; kt < 2; ++kt)
+                        if ((lv >> kt) & 1u) {
+#pragma unroll
+                            for (int i = 0; i < 16; ++i) {
+                                const float p = __builtin_amdgcn_exp2f(fmaf(s[kt][i], c2, -mc));
+                                s[kt][i] = p;
+                                lsum += p;
+                            }
+                        }
+                    return lsum;
+                };
+                scores();
+
+                // Lazy reference max.  Once every row of the wave has a reference,
+                // the tile's max is not computed: the weights are taken against the
+                // reference directly, and a per-lane sum of at most 2^8 shows that
+                // no weight exceeds 2^8 (the bound the reference is kept to).  Else
+                // (no reference yet, or a larger sum: some row's max moved up) the
+                // scores are formed again and the exact path below moves the
+                // reference to the row max, rescaling the accumulator.
+                bool exact = no_ref;
+                if (!exact) {
+                    const float lsum = weights();
+                    exact = __builtin_amdgcn_ballot_w64(!(lsum <= 256.f)) != 0;  // also catches inf
+                    if (exact)
+                        scores();
+                    else
+                        l_run += lsum;
+                }
+                if (exact) {
+                    float mx = -INFINITY;
+#pragma unroll
+                    for (int kt = 0; kt < 2; ++kt)
+                        if ((lv >> kt) & 1u) {
+#pragma unroll
+                            for (int i = 0; i < 16; ++i) mx = __builtin_fmaxf(mx, s[kt][i]);
+                        }
+                    mx = half_max(mx);
+                    const float m_new = __builtin_fmaxf(m_ref, mx);
+                    if (__builtin_amdgcn_ballot_w64(m_new > m_ref)) {
+                        const float alpha = m_new == -INFINITY ? 1.f : __builtin_amdgcn_exp2f((m_ref - m_new) * c2);
+                        l_run *= alpha;
+#pragma unroll
+                        for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+                            for (int i = 0; i < 16; ++i) oacc[dt][i] *= alpha;
+                        m_ref = m_new;
+                        mc = m_ref == -INFINITY ? 0.f : m_ref * c2;
+                    }
+                    no_ref = __builtin_amdgcn_ballot_w64(m_ref == -INFINITY) != 0;
+                    l_run += weights();
+                }
+
+                // P^T (chunk cc of P^T is registers 8*(cc%2)..+7 of s[cc/2]), then
+                // O^T += V^T P^T, one live 32-key half at a time.
+#pragma unroll
+                for (int kt = 0; kt < 2; ++kt)
+                    if ((lv >> kt) & 1u) {
                         bf16x8 vop[2][D / 32];
 #pragma unroll
                         for (int h = 0; h < 2; ++h)
@@ -232,60 +296,119 @@ __global__ __launch_bounds__(256) void fwd_bf16_t64_kernel(const FwdArgs a)
                                 vop[h][dt] = lds_read_tr8(vc + voff[0][dt] + cc * 16 * TL::kRow,
                                                           vc + voff[1][dt] + cc * 16 * TL::kRow);
                             }
-                        const bf16x8 pb[2] = {pack8(s, 0), pack8(s, 8)};
+                        const bf16x8 pb[2] = {pack8(s[kt], 0), pack8(s[kt], 8)};
 #pragma unroll
                         for (int h = 0; h < 2; ++h)
 #pragma unroll
                             for (int dt = 0; dt < D / 32; ++dt)
                                 oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop[h][dt], pb[h], oacc[dt], 0, 0, 0);
-                    };
-                    // Lazy reference: the row max of the half is taken, but the
-                    // reference m_ref (and with it the accumulator's scale) only
-                    // moves when some weight against it would exceed 2^8, or when
-                    // the row had no reference yet.  A half where each lane has at
-                    // most one allowed element (strided B's diagonal blocks) takes
-                    // that element's score x alone (-inf if the lane has none):
-                    // one exponential per lane instead of sixteen.  Otherwise the
-                    // disallowed elements of a partial half go to -inf first.
-                    float mx = -INFINITY, x = -INFINITY;
-                    if (one) {
+                    }
+            } else {
+                // Each live half is folded in on its own: S^T = K Q^T, weights,
+                // O^T += V^T P^T.  Register i of s holds key 32*kt + 8*(i/4) + 4*hh
+                // + i%4 of query n.
 #pragma unroll
-                        for (int i = 0; i < 16; ++i) x = __builtin_amdgcn_inverse_ballot_w64(pln[i]) ? s[i] : x;
-                        mx = x;
-                    } else {
+                for (int kt = 0; kt < 2; ++kt)
+                    if ((lv >> kt) & 1u) {
+                        f32x16 s;
+                        const bool partial = mid >= 0 && !((fl >> kt) & 1u);
+                        const bool one = (o1 >> kt) & 1u;  // (implies partial)
+                        // The half's 16 planes into SGPRs first, so the loads overlap
+                        // the products; then S^T = K Q^T.
+                        uint64_t pln[16];
                         if (partial) {
 #pragma unroll
-                            for (int i = 0; i < 16; ++i)
-                                s[i] = __builtin_amdgcn_inverse_ballot_w64(pln[i]) ? s[i] : -INFINITY;
+                            for (int r = 0; r < 16; ++r) pln[r] = pl[16 * kt + r];
                         }
+                        {
+                            bf16x8 kop[D / 16];
 #pragma unroll
-                        for (int i = 0; i < 16; ++i) mx = __builtin_fmaxf(mx, s[i]);
-                    }
-                    mx = half_max(mx);
-                    const bool move = fmaf(mx, c2, -mc) > 8.f;
-                    if (__builtin_amdgcn_ballot_w64(move)) {
-                        // (0 for a row's first reference: nothing is summed yet)
-                        const float alpha = move ? __builtin_amdgcn_exp2f((m_ref - mx) * c2) : 1.f;
-                        l_run *= alpha;
+                            for (int c = 0; c < D / 16; ++c) kop[c] = *(const bf16x8*)(kc + koff[c] + kt * 32 * TL::kRow);
 #pragma unroll
-                        for (int dt = 0; dt < D / 32; ++dt)
+                            for (int i = 0; i < 16; ++i) s[i] = 0.f;
 #pragma unroll
-                            for (int i = 0; i < 16; ++i) oacc[dt][i] *= alpha;
-                        if (move) {
-                            m_ref = mx;
-                            mc = mx * c2;
+                            for (int c = 0; c < D / 16; ++c)
+                                s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop[c], qop[c], s, 0, 0, 0);
                         }
-                    }
-                    if (one) {
-                        const float p = __builtin_amdgcn_exp2f(fmaf(x, c2, -mc));
-                        l_run += p;
+                        // Weights p = exp2(c2 s - mc), in place; returns this
+                        // lane's sum of them.
+                        auto weights = [&]() {
+                            float lsum = 0.f;
 #pragma unroll
-                        for (int i = 0; i < 16; ++i) s[i] = __builtin_amdgcn_inverse_ballot_w64(pln[i]) ? p : 0.f;
-                    } else {
-                        l_run += weights();
+                            for (int i = 0; i < 16; ++i) {
+                                const float p = __builtin_amdgcn_exp2f(fmaf(s[i], c2, -mc));
+                                s[i] = p;
+                                lsum += p;
+                            }
+                            return lsum;
+                        };
+                        // O^T += V^T P^T (chunk h of this half's P^T is registers
+                        // 8h..8h+7 of s).
+                        auto products = [&]() {
+                            bf16x8 vop[2][D / 32];
+#pragma unroll
+                            for (int h = 0; h < 2; ++h)
+#pragma unroll
+                                for (int dt = 0; dt < D / 32; ++dt) {
+                                    const int cc = 2 * kt + h;
+                                    vop[h][dt] = lds_read_tr8(vc + voff[0][dt] + cc * 16 * TL::kRow,
+                                                              vc + voff[1][dt] + cc * 16 * TL::kRow);
+                                }
+                            const bf16x8 pb[2] = {pack8(s, 0), pack8(s, 8)};
+#pragma unroll
+                            for (int h = 0; h < 2; ++h)
+#pragma unroll
+                                for (int dt = 0; dt < D / 32; ++dt)
+                                    oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop[h][dt], pb[h], oacc[dt], 0, 0, 0);
+                        };
+                        // Lazy reference: the row max of the half is taken, but the
+                        // reference m_ref (and with it the accumulator's scale) only
+                        // moves when some weight against it would exceed 2^8, or when
+                        // the row had no reference yet.  A half where each lane has at
+                        // most one allowed element (strided B's diagonal blocks) takes
+                        // that element's score x alone (-inf if the lane has none):
+                        // one exponential per lane instead of sixteen.  Otherwise the
+                        // disallowed elements of a partial half go to -inf first.
+                        float mx = -INFINITY, x = -INFINITY;
+                        if (one) {
+#pragma unroll
+                            for (int i = 0; i < 16; ++i) x = __builtin_amdgcn_inverse_ballot_w64(pln[i]) ? s[i] : x;
+                            mx = x;
+                        } else {
+                            if (partial) {
+#pragma unroll
+                                for (int i = 0; i < 16; ++i)
+                                    s[i] = __builtin_amdgcn_inverse_ballot_w64(pln[i]) ? s[i] : -INFINITY;
+                            }
+#pragma unroll
+                            for (int i = 0; i < 16; ++i) mx = __builtin_fmaxf(mx, s[i]);
+                        }
+                        mx = half_max(mx);
+                        const bool move = fmaf(mx, c2, -mc) > 8.f;
+                        if (__builtin_amdgcn_ballot_w64(move)) {
+                            // (0 for a row's first reference: nothing is summed yet)
+                            const float alpha = move ? __builtin_amdgcn_exp2f((m_ref - mx) * c2) : 1.f;
+                            l_run *= alpha;
+#pragma unroll
+                            for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+                                for (int i = 0; i < 16; ++i) oacc[dt][i] *= alpha;
+                            if (move) {
+                                m_ref = mx;
+                                mc = mx * c2;
+                            }
+                        }
+                        if (one) {
+                            const float p = __builtin_amdgcn_exp2f(fmaf(x, c2, -mc));
+                            l_run += p;
+#pragma unroll
+                            for (int i = 0; i < 16; ++i) s[i] = __builtin_amdgcn_inverse_ballot_w64(pln[i]) ? p : 0.f;
+                        } else {
+                            l_run += weights();
+                        }
+                        products();
                     }
-                    products();
-                }
+            }
         }  // this wave's block lists the key block
         wait_vmem();      // tile t + 1 has landed ...
         __syncthreads();  // ... for every wave, and every wave is done with tile t
@@ -409,12 +532,17 @@ __global__ __launch_bounds__(64) void fwd_f32_t16_d64_kernel(const FwdArgs a)
 
 }  // namespace
 
-hipError_t launch_fwd_bf16_t64(int d, const FwdArgs& a, int n_items, hipStream_t stream)
+hipError_t launch_fwd_bf16_t64(int d, const FwdArgs& a, int n_items, bool paired, hipStream_t stream)
 {
-    if (d == 64)
-        hipLaunchKernelGGL(fwd_bf16_t64_kernel<64>, dim3(n_items), dim3(256), 0, stream, a);
+    const dim3 g(n_items), b(256);
+    if (d == 64 && paired)
+        hipLaunchKernelGGL((fwd_bf16_t64_kernel<64, true>), g, b, 0, stream, a);
+    else if (d == 64)
+        hipLaunchKernelGGL((fwd_bf16_t64_kernel<64, false>), g, b, 0, stream, a);
+    else if (paired)
+        hipLaunchKernelGGL((fwd_bf16_t64_kernel<128, true>), g, b, 0, stream, a);
     else
-        hipLaunchKernelGGL(fwd_bf16_t64_kernel<128>, dim3(n_items), dim3(256), 0, stream, a);
+        hipLaunchKernelGGL((fwd_bf16_t64_kernel<128, false>), g, b, 0, stream, a);
     return hipGetLastError();
 }
 

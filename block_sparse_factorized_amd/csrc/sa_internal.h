@@ -121,6 +121,9 @@ struct sa_layout {
     // Some partial quadrant leaves each lane of the forward's score layout
     // at most one allowed element (set when the layout is first uploaded).
     bool one_quads = false;
+    // Wave-steps of the forward's walk with both 32-key halves live (not both
+    // of one element per lane) and with one live half (set at upload).
+    int64_t fwd_pair_steps = 0, fwd_half_steps = 0;
 
     std::mutex mu;                       // guards dev
     std::map<int, void*> dev_mem;        // device id -> allocation
