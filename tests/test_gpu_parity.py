@@ -209,17 +209,27 @@ def _ramp_inputs(kind, n, d, seed):
     return {"q": t(q), "k": t(k), "v": t(v), "do": t(do)}
 
 
+RAMP_PATTERNS = {
+    # mostly full blocks: the forward's two-half form
+    "full": [("dense", 1, 1), ("dense", 1, 1), ("strided_a", 512, 1), ("fixed_a", 256, 1)],
+    # mostly one live half per step: the per-half form
+    "sparse": [("strided_b", 128, 1), ("fixed_b", 128, 32), ("strided_b", 64, 1), ("strided_a", 64, 1)],
+}
+
+
 @pytest.mark.parametrize("kind", ["rising", "falling", "spikes"])
-def test_running_reference_moves(kind):
-    """The forward's running reference: rows whose max keeps rising along the
-    walk, rows whose max comes first, and far-out spikes.  Forward only: on
-    these inputs dQ is a small difference of large terms, and rounding dS to
-    bf16 for the product alone moves it by 6-13 % (relative L2) from the
-    exact value, past the gradient bar, whatever the kernel does."""
+@pytest.mark.parametrize("family", ["full", "sparse"])
+def test_running_reference_moves(kind, family):
+    """The forward's running reference, in both of its forms: rows whose max
+    keeps rising along the walk, rows whose max comes first, and far-out
+    spikes.  Forward only: on these inputs dQ is a small difference of large
+    terms, and rounding dS to bf16 for the product alone moves it by 6-13 %
+    (relative L2) from the exact value, past the gradient bar, whatever the
+    kernel does."""
     n, d = 1024, 64
     x = _ramp_inputs(kind, n, d, seed=5)
     scale = 1.0 / math.sqrt(d)
-    pats = [("dense", 1, 1), ("strided_b", 128, 1), ("fixed_b", 128, 32), ("strided_a", 128, 1)]
+    pats = RAMP_PATTERNS[family]
     res = run(x, pats, 64, scale, backward=False)
     assert torch.isfinite(res["o"]).all()
     for h in range(4):
