@@ -50,7 +50,7 @@ class SAError(RuntimeError):
 def _load():
     if not os.path.exists(LIB_PATH):
         raise ImportError("libsa.so is not built (%s); run __graft_entry__.build() or "
-                          "python -m block_sparse_factorized_amd._build" % LIB_PATH)
+                          "python block_sparse_factorized_amd/_build.py" % LIB_PATH)
     lib = ctypes.CDLL(LIB_PATH)
     i32, i64, vp, cint, flt = ctypes.c_int32, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int, ctypes.c_float
     sz = ctypes.c_size_t
