@@ -7,6 +7,7 @@ fails if the library has not been built.
 """
 from ._binding import (  # noqa: F401
     EXPORTED,
+    FWD_FORMS,
     LIB_PATH,
     PATTERNS,
     SA_BF16,
@@ -33,5 +34,6 @@ from ._binding import (  # noqa: F401
     sa_layout_set_compact_view,
     sa_layout_set_residue_view,
     sa_layout_view_info,
+    sa_set_fwd_form,
     sparse_attention,
 )

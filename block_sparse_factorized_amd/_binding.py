@@ -36,7 +36,7 @@ EXPORTED = [
     "sa_layout_build", "sa_layout_info", "sa_layout_export", "sa_layout_set_residue_view",
     "sa_layout_set_compact_view", "sa_layout_view_info", "sa_layout_destroy",
     "sa_fwd", "sa_bwd", "sa_bwd_workspace_size", "sa_bwd_dq_rowterms", "sa_bwd_rowterms", "sa_bwd_dkdv",
-    "sa_bwd_dq",
+    "sa_bwd_dq", "sa_set_fwd_form",
     "sa_status_string", "sa_last_error",
 ]
 
@@ -82,6 +82,8 @@ def _load():
     lib.sa_bwd_dq_rowterms.restype = cint
     lib.sa_bwd_dq.argtypes = [vp, i32, i32, i64, i32, cint, flt] + [vp] * 6 + [sz, vp]
     lib.sa_bwd_dq.restype = cint
+    lib.sa_set_fwd_form.argtypes = [cint]
+    lib.sa_set_fwd_form.restype = cint
     lib.sa_status_string.argtypes = [cint]
     lib.sa_status_string.restype = ctypes.c_char_p
     lib.sa_last_error.argtypes = []
@@ -173,6 +175,19 @@ class Layout:
             pass
 
 
+FWD_FORMS = {"auto": 0, "half": 1, "paired": 2}
+
+
+def sa_set_fwd_form(form: Union[str, int]) -> str:
+    """Process-wide forward kernel form ("auto", "half" or "paired"; see
+    sa_set_fwd_form in sa.h).  Returns the previous setting."""
+    code = FWD_FORMS[form] if isinstance(form, str) else int(form)
+    prev = _lib.sa_set_fwd_form(code)
+    if prev < 0:
+        _check(prev)
+    return {v: k for k, v in FWD_FORMS.items()}[prev]
+
+
 def sa_layout_build(pattern: Union[str, int], n: int, l: int, c: int = 1, block: int = 64) -> Layout:
     pid = PATTERNS[pattern] if isinstance(pattern, str) else int(pattern)
     h = ctypes.c_void_p()
@@ -232,6 +247,17 @@ def _stream_handle(stream, device):
     return ctypes.c_void_p(s.cuda_stream)
 
 
+def _on_stream(stream):
+    """Context in which the binding allocates the outputs and the workspace
+    of a call: the stream the call's kernels run on.  torch's caching
+    allocator ties a block to the stream it was allocated on, so a workspace
+    freed when the call returns is reused only by later work on that same
+    stream, which runs after the kernels that read it."""
+    import contextlib
+    import torch
+    return torch.cuda.stream(stream) if stream is not None else contextlib.nullcontext()
+
+
 def _check_tensor(name, t, shape, dtype, device):
     if tuple(t.shape) != tuple(shape) or t.dtype != dtype or t.device != device or not t.is_contiguous():
         raise ValueError("%s must be a contiguous %s tensor of shape %s on %s" % (name, dtype, shape, device))
@@ -245,10 +271,11 @@ def sa_fwd(q, k, v, layouts: Union[Layout, Sequence[Layout]], scale: float, o=No
     for name, t in (("k", k), ("v", v)):
         _check_tensor(name, t, q.shape, q.dtype, q.device)
     _check_tensor("q", q, q.shape, q.dtype, q.device)
-    if o is None:
-        o = torch.empty_like(q)
-    if lse is None:
-        lse = torch.empty((B, H, n), dtype=torch.float32, device=q.device)
+    with _on_stream(stream):
+        if o is None:
+            o = torch.empty_like(q)
+        if lse is None:
+            lse = torch.empty((B, H, n), dtype=torch.float32, device=q.device)
     _check_tensor("o", o, q.shape, q.dtype, q.device)
     _check_tensor("lse", lse, (B, H, n), torch.float32, q.device)
     heads = _head_array(layouts, H)
@@ -265,14 +292,15 @@ def sa_bwd(q, k, v, o, lse, do, layouts: Union[Layout, Sequence[Layout]], scale:
     for name, t in (("q", q), ("k", k), ("v", v), ("o", o), ("do", do)):
         _check_tensor(name, t, q.shape, q.dtype, q.device)
     _check_tensor("lse", lse, (B, H, n), torch.float32, q.device)
-    dq = torch.empty_like(q) if dq is None else dq
-    dk = torch.empty_like(q) if dk is None else dk
-    dv = torch.empty_like(q) if dv is None else dv
+    ws_bytes = sa_bwd_workspace_size(B, H, n, d)
+    with _on_stream(stream):
+        dq = torch.empty_like(q) if dq is None else dq
+        dk = torch.empty_like(q) if dk is None else dk
+        dv = torch.empty_like(q) if dv is None else dv
+        if workspace is None:
+            workspace = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=q.device)
     for name, t in (("dq", dq), ("dk", dk), ("dv", dv)):
         _check_tensor(name, t, q.shape, q.dtype, q.device)
-    ws_bytes = sa_bwd_workspace_size(B, H, n, d)
-    if workspace is None:
-        workspace = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=q.device)
     heads = _head_array(layouts, H)
     _check(_lib.sa_bwd(heads, B, H, n, d, _dtype_code(q), float(scale), q.data_ptr(), k.data_ptr(),
                        v.data_ptr(), o.data_ptr(), lse.data_ptr(), do.data_ptr(), dq.data_ptr(),
@@ -315,12 +343,13 @@ def _sparse_attention_fn():
     return _SPARSE_ATTENTION_FN
 
 
-def _bwd_common(q, layouts, workspace):
+def _bwd_common(q, layouts, workspace, stream):
     import torch
     B, H, n, d = q.shape
     ws_bytes = sa_bwd_workspace_size(B, H, n, d)
     if workspace is None:
-        workspace = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=q.device)
+        with _on_stream(stream):
+            workspace = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=q.device)
     return B, H, n, d, _head_array(layouts, H), workspace
 
 
@@ -330,9 +359,10 @@ def sa_bwd_dq_rowterms(q, k, v, o, lse, do, layouts, scale: float, workspace=Non
     import torch
     for name, t in (("k", k), ("v", v), ("o", o), ("do", do)):
         _check_tensor(name, t, q.shape, q.dtype, q.device)
-    B, H, n, d, heads, workspace = _bwd_common(q, layouts, workspace)
+    B, H, n, d, heads, workspace = _bwd_common(q, layouts, workspace, stream)
     _check_tensor("lse", lse, (B, H, n), torch.float32, q.device)
-    dq = torch.empty_like(q) if dq is None else dq
+    with _on_stream(stream):
+        dq = torch.empty_like(q) if dq is None else dq
     _check_tensor("dq", dq, q.shape, q.dtype, q.device)
     _check(_lib.sa_bwd_dq_rowterms(heads, B, H, n, d, _dtype_code(q), float(scale), q.data_ptr(), k.data_ptr(),
                                    v.data_ptr(), o.data_ptr(), lse.data_ptr(), do.data_ptr(), dq.data_ptr(),
@@ -345,7 +375,7 @@ def sa_bwd_rowterms(o, lse, do, layouts, scale: float, workspace=None, stream=No
     into ``workspace`` (allocated and returned when None)."""
     import torch
     _check_tensor("do", do, o.shape, o.dtype, o.device)
-    B, H, n, d, heads, workspace = _bwd_common(o, layouts, workspace)
+    B, H, n, d, heads, workspace = _bwd_common(o, layouts, workspace, stream)
     _check_tensor("lse", lse, (B, H, n), torch.float32, o.device)
     _check(_lib.sa_bwd_rowterms(heads, B, H, n, d, _dtype_code(o), float(scale), o.data_ptr(), lse.data_ptr(),
                                 do.data_ptr(), workspace.data_ptr(), workspace.numel(),
@@ -358,9 +388,10 @@ def sa_bwd_dkdv(q, k, v, do, layouts, scale: float, workspace, dk=None, dv=None,
     import torch
     for name, t in (("k", k), ("v", v), ("do", do)):
         _check_tensor(name, t, q.shape, q.dtype, q.device)
-    B, H, n, d, heads, workspace = _bwd_common(q, layouts, workspace)
-    dk = torch.empty_like(q) if dk is None else dk
-    dv = torch.empty_like(q) if dv is None else dv
+    B, H, n, d, heads, workspace = _bwd_common(q, layouts, workspace, stream)
+    with _on_stream(stream):
+        dk = torch.empty_like(q) if dk is None else dk
+        dv = torch.empty_like(q) if dv is None else dv
     for name, t in (("dk", dk), ("dv", dv)):
         _check_tensor(name, t, q.shape, q.dtype, q.device)
     _check(_lib.sa_bwd_dkdv(heads, B, H, n, d, _dtype_code(q), float(scale), q.data_ptr(), k.data_ptr(),
@@ -374,8 +405,9 @@ def sa_bwd_dq(q, k, v, do, layouts, scale: float, workspace, dq=None, stream=Non
     import torch
     for name, t in (("k", k), ("v", v), ("do", do)):
         _check_tensor(name, t, q.shape, q.dtype, q.device)
-    B, H, n, d, heads, workspace = _bwd_common(q, layouts, workspace)
-    dq = torch.empty_like(q) if dq is None else dq
+    B, H, n, d, heads, workspace = _bwd_common(q, layouts, workspace, stream)
+    with _on_stream(stream):
+        dq = torch.empty_like(q) if dq is None else dq
     _check_tensor("dq", dq, q.shape, q.dtype, q.device)
     _check(_lib.sa_bwd_dq(heads, B, H, n, d, _dtype_code(q), float(scale), q.data_ptr(), k.data_ptr(),
                           v.data_ptr(), do.data_ptr(), dq.data_ptr(), workspace.data_ptr(),

@@ -14,7 +14,7 @@ CSRC = os.path.join(HERE, "csrc")
 OUT_DIR = os.path.join(HERE, "_lib")
 OBJ_DIR = os.path.join(HERE, "_build")
 LIB = os.path.join(OUT_DIR, "libsa.so")
-SOURCES = ["layout.cpp", "capi.cpp", "fwd.hip", "bwd.hip"]
+SOURCES = ["layout.cpp", "pack.cpp", "capi.cpp", "fwd.hip", "bwd.hip"]
 # libsa_peaks.so: the micro-benchmarks of include/sa_peaks.h (not part of libsa)
 PEAKS_LIB = os.path.join(OUT_DIR, "libsa_peaks.so")
 PEAKS_SOURCES = ["peaks.hip"]
@@ -51,7 +51,7 @@ def _link(objs, lib: str) -> None:
 def build(verbose: bool = False) -> str:
     os.makedirs(OUT_DIR, exist_ok=True)
     os.makedirs(OBJ_DIR, exist_ok=True)
-    with ThreadPoolExecutor(max_workers=min(5, len(SOURCES) + len(PEAKS_SOURCES))) as ex:
+    with ThreadPoolExecutor(max_workers=min(6, len(SOURCES) + len(PEAKS_SOURCES))) as ex:
         objs = list(ex.map(_compile, SOURCES + PEAKS_SOURCES))
     _link(objs[:len(SOURCES)], LIB)
     _link(objs[len(SOURCES):], PEAKS_LIB)

@@ -15,13 +15,34 @@
 // written row by row without testing every element.  Key blocks that cannot
 // hold a pair are skipped by a per-pattern range or test first.
 #include <algorithm>
+#include <cstdarg>
+#include <cstdio>
 #include <cstring>
 #include <new>
+#include <string>
 #include <unordered_map>
 
 #include "sa_internal.h"
 
 namespace sa {
+
+namespace {
+thread_local std::string g_last_error;
+}
+
+int fail(int status, const char* fmt, ...)
+{
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_last_error = buf;
+    return status;
+}
+
+const char* last_error() { return g_last_error.c_str(); }
+
 namespace {
 
 struct Params {
@@ -277,6 +298,28 @@ int build_layout(int pattern, int64_t n, int64_t l, int64_t c, int32_t block, sa
         return fail(SA_ERR_ALLOC, "sa_layout_build: out of host memory");
     }
     *out = L;
+    return SA_OK;
+}
+
+// Residue view of strided B with stride l (n % l == 0, block 64): position
+// i attends exactly the earlier positions of its residue class i mod l
+// (pcnews.ru, "Разреженное внимание": attention along a column is attention
+// along a row of the transposed matrix), so the kernels walk one dense
+// causal layout over m = n / l rows (rounded up to blocks), once per residue
+// class, reading rows l apart.
+int build_residue_view(int64_t n, int64_t l, sa_layout** out)
+{
+    *out = nullptr;
+    if (l < 1 || n % l != 0)
+        return fail(SA_ERR_UNSUPPORTED, "residue view: needs n %% l == 0");
+    const int64_t m = n / l, m_pad = (m + 63) / 64 * 64;
+    sa_layout* rv = nullptr;
+    int st = build_layout(SA_DENSE_CAUSAL, m_pad, 1, 0, 64, &rv);
+    if (st != SA_OK) return st;
+    rv->view_l = l;
+    rv->view_m = m;
+    rv->key_m = m;
+    *out = rv;
     return SA_OK;
 }
 

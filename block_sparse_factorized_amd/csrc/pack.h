@@ -1,0 +1,44 @@
+// pack.h -- host side of what libsa uploads: the device image of a layout
+// and the work lists of a call, built in host memory with no HIP calls (so
+// that they can also be built and checked on the CPU alone).
+#pragma once
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <vector>
+
+#include "kernel_args.h"
+#include "sa_internal.h"
+
+namespace sa {
+
+// A layout's device copy as one host buffer of 256-byte aligned sections,
+// and where each section starts (see DevLayout for what they hold).
+struct LayoutImage {
+    std::vector<unsigned char> host;
+    size_t off_masks, off_masks_t, off_planes, off_planes_t;
+    size_t off_row_ptr, off_col_idx, off_mask_id, off_col_ptr, off_row_idx, off_col_mask;
+    size_t off_gptr[2], off_gblk[2], off_gstep[2];
+    size_t off_kmode;
+    bool has_planes;  // block 64: lane-mask planes present
+};
+
+// Builds the image of L (and sets L's upload-time summaries: one_quads,
+// fwd_pair_steps, fwd_half_steps).  Returns SA_OK.
+int pack_layout(sa_layout* L, LayoutImage* img);
+
+// The device view of an image copied to device address `base`.
+DevLayout place_layout(const LayoutImage& img, const sa_layout* L, const unsigned char* base);
+
+// What a work list's items walk: query blocks (fp32 forward), query-block
+// pairs (bf16 forward, dQ) or key-block pairs (dK/dV).
+enum ListKind { kByQuery = 0, kByQueryPair = 1, kByKeyPair = 2 };
+
+// The work items of a call over B batches and H heads (layout hl[h] for
+// head h): one per (batch*head, block or pair, residue class), longest list
+// first, so the heaviest items start early and the tail is made of short
+// ones.
+void build_work_items(ListKind kind, int32_t B, int32_t H, sa_layout* const* hl, std::vector<Item>* out);
+
+}  // namespace sa

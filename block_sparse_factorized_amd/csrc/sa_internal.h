@@ -134,11 +134,14 @@ namespace sa {
 
 // Layout builder (host only, layout.cpp).
 int build_layout(int pattern, int64_t n, int64_t l, int64_t c, int32_t block, sa_layout** out);
-// The compact view of fixed B (block 64; n % l == 0, c a power of two).
+// The residue view of strided B (block 64; n % l == 0) and the compact view
+// of fixed B (block 64; n % l == 0, c a power of two).
+int build_residue_view(int64_t n, int64_t l, sa_layout** out);
 int build_compact_view(int64_t n, int64_t l, int64_t c, sa_layout** out);
 
-// Error reporting (capi.cpp): records the message for sa_last_error and
-// returns `status`.
+// Error reporting (layout.cpp): records the message for sa_last_error and
+// returns `status`; last_error() is the calling thread's last message.
 int fail(int status, const char* fmt, ...);
+const char* last_error();
 
 }  // namespace sa

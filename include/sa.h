@@ -95,7 +95,12 @@ typedef struct sa_layout sa_layout_t;
 /*
  * Build the block layout of `pattern` for sequence length n, stride l,
  * summary width c (used by SA_FIXED_B only) and block size `block`.
- * Host only.  For every query block qb (rows qb*block .. qb*block+block-1)
+ * Source: "OpenAI Sparse Transformer", "Implementation and Limitations", and
+ * pcnews.ru, "Релиз кода": the query and key matrices are cut into blocks
+ * and only the blocks the pattern needs are computed; "희소 어텐션 (Sparse
+ * Attention)": the block size is the granularity of the sparsity; the
+ * predicates themselves are those of "Factorized Attention Patterns" (file
+ * head).  Host only.  For every query block qb (rows qb*block .. qb*block+block-1)
  * it lists, in ascending order, every key block kb holding at least one
  * allowed (i, j), and gives each listed block an element mask: -1 when every
  * element is allowed ("full"), else the index of a T*T-bit mask in a
@@ -193,7 +198,14 @@ int sa_layout_view_info(const sa_layout_t* lay, int* kind, int64_t* nqb, int64_t
 void sa_layout_destroy(sa_layout_t* lay);
 
 /*
- * Forward pass.  head_layout[h] (h < H) is the layout of head h; several
+ * Forward pass.  Source: "희소 어텐션 (Sparse Attention)": per head, the
+ * scores are dot products of the queries with the keys and a softmax turns
+ * each row of scores into weights that sum to one, which average the
+ * values; "OpenAI Sparse Transformer", "Sparse Attention and Algorithmic
+ * Complexity": only the layout's allowed (query, key) pairs enter a row;
+ * "[논문 리뷰] Generating Long Sequences with Sparse Transformers", ABSTRACT
+ * (b): the row log-sum-exp is kept so that the backward pass can rebuild
+ * the weights.  head_layout[h] (h < H) is the layout of head h; several
  * heads may share one layout, at most 8 distinct layouts per call, H <= 256.
  * Every layout must have sequence length n and the call's block size
  * (16 for SA_F32, 64 for SA_BF16).  scale must be finite and > 0.
@@ -208,11 +220,20 @@ int sa_fwd(const sa_layout_t* const* head_layout, int32_t B, int32_t H, int64_t 
            float* lse, void* stream);
 
 /* Bytes of device workspace sa_bwd needs: two fp32 row terms per row,
- * -D_i = -sum_t dO_it O_it and -lse_i * log2(e). */
+ * -D_i = -sum_t dO_it O_it and -lse_i * log2(e).  Source: "[논문 리뷰]
+ * Generating Long Sequences with Sparse Transformers", ABSTRACT (b): the
+ * backward pass rebuilds the weights from what the forward pass kept (O and
+ * lse) instead of storing them; these two per-row terms are all it derives
+ * from O and lse, 8 bytes per row (0 when B, H or n < 1). */
 size_t sa_bwd_workspace_size(int32_t B, int32_t H, int64_t n, int32_t d);
 
 /*
  * Backward pass (recomputes the attention weights from q, k and lse).
+ * Source: "[논문 리뷰] Generating Long Sequences with Sparse Transformers"
+ * (nubint.ai), ABSTRACT (b) and "제안 방법", and pcnews.ru, "Глубокое
+ * внимание": the attention matrices are recomputed during backpropagation
+ * rather than stored; the gradients are those of the forward's definition
+ * over the same allowed pairs.
  * o and lse are sa_fwd's outputs for the same inputs; dout is dL/dO.
  * Writes dq, dk, dv [B][H][n][d] (dtype).  workspace: device memory of at
  * least sa_bwd_workspace_size(...) bytes, 16-byte aligned, owned by the
@@ -258,6 +279,22 @@ int sa_bwd_dkdv(const sa_layout_t* const* head_layout, int32_t B, int32_t H, int
 int sa_bwd_dq(const sa_layout_t* const* head_layout, int32_t B, int32_t H, int64_t n, int32_t d,
               int dtype, float scale, const void* q, const void* k, const void* v, const void* dout,
               void* dq, const void* workspace, size_t ws_bytes, void* stream);
+
+/*
+ * Forward kernel form, process-wide: a tuning and testing switch (both forms
+ * compute the same attention; their results differ only in rounding order).
+ *   0  chosen per call (default): the two-half form when most wave-steps of
+ *      the call's walk have both 32-key halves of a block live, else the
+ *      per-half form
+ *   1  the per-half form: each live 32-key half is scored and folded into
+ *      the running softmax on its own
+ *   2  the two-half form: a step's live halves are scored together and the
+ *      running reference is checked once per step
+ * Applies to bf16 calls (the fp32 kernel has one form).  Returns the
+ * previous setting, or SA_ERR_INVALID_ARG (setting unchanged) for another
+ * value.  Calls of sa_fwd that are already enqueued are not affected.
+ */
+int sa_set_fwd_form(int form);
 
 /* Static text of a status code. */
 const char* sa_status_string(int status);

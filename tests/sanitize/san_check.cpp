@@ -1,0 +1,156 @@
+// san_check.cpp -- libsa's host code under AddressSanitizer and
+// UndefinedBehaviorSanitizer (built by tests/test_sanitize.py with g++ on
+// the CPU; no GPU, no HIP runtime): the layout builder, the residue and
+// compact views, the device image of every layout (listings, mask tables,
+// lane-mask planes, block pairs and their step records, key-pair modes) and
+// the work lists, over seeded random layouts and the full-size workloads.
+// Each image is also checked for self-consistency: its sections lie inside
+// the buffer, in order, and the step records point at valid masks.
+// Exit status 0 when every check passes (a sanitizer report aborts).
+#include <cstdio>
+#include <cstdlib>
+#include <vector>
+
+#include "pack.h"
+#include "sa_internal.h"
+
+using namespace sa;
+
+namespace {
+
+uint64_t g_state = 0x5eed5eed2019ull;
+uint64_t next()  // splitmix64
+{
+    uint64_t z = (g_state += 0x9e3779b97f4a7c15ull);
+    z = (z ^ (z >> 30)) * 0xbf58476d1ce4e5b9ull;
+    z = (z ^ (z >> 27)) * 0x94d049bb133111ebull;
+    return z ^ (z >> 31);
+}
+int64_t pick(int64_t lo, int64_t hi) { return lo + (int64_t)(next() % (uint64_t)(hi - lo + 1)); }
+
+int g_fail = 0;
+#define CHECK(cond, ...)                                 \
+    do {                                                 \
+        if (!(cond)) {                                   \
+            std::fprintf(stderr, "check failed: " #cond " -- " __VA_ARGS__); \
+            std::fprintf(stderr, "\n");                  \
+            ++g_fail;                                    \
+        }                                                \
+    } while (0)
+
+void check_image(sa_layout* L, const char* what)
+{
+    LayoutImage img;
+    CHECK(pack_layout(L, &img) == SA_OK, "%s", what);
+    const size_t total = img.host.size();
+    const size_t offs[] = {img.off_masks, img.off_masks_t, img.off_planes, img.off_planes_t, img.off_row_ptr,
+                           img.off_col_idx, img.off_mask_id, img.off_col_ptr, img.off_row_idx, img.off_col_mask,
+                           img.off_gptr[0], img.off_gblk[0], img.off_gstep[0], img.off_gptr[1], img.off_gblk[1],
+                           img.off_gstep[1], img.off_kmode};
+    for (size_t a = 0; a < sizeof offs / sizeof offs[0]; ++a) {
+        CHECK(offs[a] % 256 == 0 && offs[a] <= total, "%s: section %zu at %zu of %zu", what, a, offs[a], total);
+        if (a) CHECK(offs[a] >= offs[a - 1], "%s: section %zu out of order", what, a);
+    }
+    CHECK(img.has_planes == (L->T == 64), "%s", what);
+    const DevLayout v = place_layout(img, L, img.host.data());
+    // Every step record names a mask that exists (or -1 full, -2 absent)
+    // and a block inside the layout.
+    for (int k = 0; k < 2; ++k) {
+        const Groups& g = k == 0 ? L->qgroups : L->kgroups;
+        const int32_t* ptr = k == 0 ? v.qgrp_ptr : v.kgrp_ptr;
+        const int4* st = k == 0 ? v.qgrp_step : v.kgrp_step;
+        const int64_t ng = (int64_t)g.ptr.size() - 1;
+        for (int64_t gi = 0; gi < ng; ++gi)
+            for (int32_t x = ptr[gi]; x < ptr[gi + 1]; ++x) {
+                CHECK(st[x].x >= 0 && st[x].x < (k == 0 ? L->nkb : L->nqb), "%s: step block %d", what, st[x].x);
+                CHECK(st[x].y >= -2 && st[x].y < L->n_masks, "%s: mask a %d", what, st[x].y);
+                CHECK(st[x].z >= -2 && st[x].z < L->n_masks, "%s: mask b %d", what, st[x].z);
+            }
+    }
+    for (ListKind kind : {kByQuery, kByQueryPair, kByKeyPair})
+        for (int32_t B : {1, 3}) {
+            sa_layout* hl[2] = {L, L};
+            std::vector<Item> items;
+            build_work_items(kind, B, 2, hl, &items);
+            const size_t per = kind == kByQuery ? L->row_ptr.size() - 1
+                               : kind == kByQueryPair ? L->qgroups.ptr.size() - 1
+                                                      : L->kgroups.ptr.size() - 1;
+            CHECK(items.size() == (size_t)B * 2 * per * (size_t)L->view_l, "%s: %zu items", what, items.size());
+            for (const Item& it : items)
+                CHECK(it.bh >= 0 && it.bh < B * 2 && it.blk >= 0 && (size_t)it.blk < per && it.r >= 0 &&
+                          it.r < L->view_l,
+                      "%s: item", what);
+        }
+}
+
+void run_case(int pattern, int64_t n, int64_t l, int64_t c, int32_t T)
+{
+    char what[160];
+    std::snprintf(what, sizeof what, "pattern %d n %lld l %lld c %lld T %d", pattern, (long long)n, (long long)l,
+                  (long long)c, T);
+    sa_layout* L = nullptr;
+    const int st = build_layout(pattern, n, l, c, T, &L);
+    CHECK(st == SA_OK, "%s: build %d (%s)", what, st, last_error());
+    if (st != SA_OK) return;
+    CHECK((int64_t)L->row_ptr.size() == L->nqb + 1 && L->row_ptr.back() == L->nnz, "%s", what);
+    check_image(L, what);
+    if (T == 64 && pattern == SA_STRIDED_B && n % l == 0) {
+        sa_layout* rv = nullptr;
+        CHECK(build_residue_view(n, l, &rv) == SA_OK, "%s: residue view", what);
+        if (rv) {
+            // l classes of a dense causal attention over n / l rows: the same pairs
+            const int64_t m = n / l;
+            CHECK(rv->allowed >= m * (m + 1) / 2, "%s: residue view pairs", what);
+            check_image(rv, what);
+            delete rv;
+        }
+    }
+    if (T == 64 && pattern == SA_FIXED_B && n % l == 0 && (c & (c - 1)) == 0) {
+        sa_layout* cv = nullptr;
+        CHECK(build_compact_view(n, l, c, &cv) == SA_OK, "%s: compact view", what);
+        if (cv) {
+            CHECK(cv->allowed == L->allowed, "%s: compact view pairs %lld vs %lld", what, (long long)cv->allowed,
+                  (long long)L->allowed);
+            check_image(cv, what);
+            delete cv;
+        }
+    }
+    delete L;
+}
+
+}  // namespace
+
+int main(int argc, char** argv)
+{
+    const int count = argc > 1 ? std::atoi(argv[1]) : 200;
+    // Seeded random layouts: every pattern, block sizes of the kernels and of
+    // the builder, strides and summary widths anywhere in range.
+    const int32_t blocks[] = {8, 16, 32, 64, 64, 64, 128};
+    for (int a = 0; a < count; ++a) {
+        const int pattern = (int)pick(0, 4);
+        const int32_t T = blocks[pick(0, 6)];
+        const int64_t n = T * pick(1, T == 64 ? 48 : 24);
+        const int64_t l = pick(0, 3) == 0 ? pick(1, 2 * n) : (int64_t)1 << pick(0, 8);
+        int64_t c = pattern == SA_FIXED_B ? pick(1, l) : 1;
+        if (pattern == SA_FIXED_B && pick(0, 1)) c = std::min<int64_t>(l, (int64_t)1 << pick(0, 7));
+        run_case(pattern, n, l, c, T);
+    }
+    // The workloads' layouts at full size (block 64).
+    run_case(SA_STRIDED_A, 3072, 128, 1, 64);
+    run_case(SA_STRIDED_B, 3072, 128, 1, 64);
+    run_case(SA_FIXED_A, 12288, 128, 32, 64);
+    run_case(SA_FIXED_B, 12288, 128, 32, 64);
+    run_case(SA_STRIDED_A, 12288, 128, 1, 64);
+    run_case(SA_STRIDED_B, 12288, 128, 1, 64);
+    run_case(SA_DENSE_CAUSAL, 12288, 1, 1, 64);
+    run_case(SA_STRIDED_A, 65536, 256, 1, 64);
+    run_case(SA_STRIDED_B, 65536, 256, 1, 64);
+    // Rejected arguments return errors, and write nothing.
+    sa_layout* L = nullptr;
+    CHECK(build_layout(SA_FIXED_B, 256, 16, 17, 64, &L) == SA_ERR_INVALID_ARG && L == nullptr, "c > l");
+    CHECK(build_layout(SA_STRIDED_A, 100, 16, 1, 64, &L) == SA_ERR_INVALID_ARG && L == nullptr, "n % block");
+    CHECK(build_residue_view(1000, 7, &L) == SA_ERR_UNSUPPORTED && L == nullptr, "residue n % l");
+    CHECK(build_compact_view(1024, 128, 24, &L) == SA_ERR_UNSUPPORTED && L == nullptr, "compact c not 2^k");
+    std::printf("%d cases, %d failed checks\n", count + 9, g_fail);
+    return g_fail ? 1 : 0;
+}
