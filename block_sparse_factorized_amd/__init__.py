@@ -24,6 +24,7 @@ from ._binding import (  # noqa: F401
     sa_bwd_dkdv,
     sa_bwd_dq,
     sa_bwd_dq_rowterms,
+    sa_bwd_noalloc,
     sa_bwd_rowterms,
     sa_bwd_workspace_size,
     sa_fwd,

@@ -36,7 +36,7 @@ EXPORTED = [
     "sa_layout_build", "sa_layout_info", "sa_layout_export", "sa_layout_set_residue_view",
     "sa_layout_set_compact_view", "sa_layout_view_info", "sa_layout_destroy",
     "sa_fwd", "sa_bwd", "sa_bwd_workspace_size", "sa_bwd_dq_rowterms", "sa_bwd_rowterms", "sa_bwd_dkdv",
-    "sa_bwd_dq", "sa_set_fwd_form",
+    "sa_bwd_dq", "sa_bwd_noalloc", "sa_set_fwd_form",
     "sa_status_string", "sa_last_error",
 ]
 
@@ -82,6 +82,8 @@ def _load():
     lib.sa_bwd_dq_rowterms.restype = cint
     lib.sa_bwd_dq.argtypes = [vp, i32, i32, i64, i32, cint, flt] + [vp] * 6 + [sz, vp]
     lib.sa_bwd_dq.restype = cint
+    lib.sa_bwd_noalloc.argtypes = [vp, i32, i32, i64, i32, cint, flt] + [vp] * 10
+    lib.sa_bwd_noalloc.restype = cint
     lib.sa_set_fwd_form.argtypes = [cint]
     lib.sa_set_fwd_form.restype = cint
     lib.sa_status_string.argtypes = [cint]
@@ -306,6 +308,23 @@ def sa_bwd(q, k, v, o, lse, do, layouts: Union[Layout, Sequence[Layout]], scale:
                        v.data_ptr(), o.data_ptr(), lse.data_ptr(), do.data_ptr(), dq.data_ptr(),
                        dk.data_ptr(), dv.data_ptr(), workspace.data_ptr(), workspace.numel(),
                        _stream_handle(stream, q.device)))
+    return dq, dk, dv
+
+
+def sa_bwd_noalloc(q, k, v, o, lse, do, layouts: Union[Layout, Sequence[Layout]], scale: float,
+                   dq, dk, dv, stream=None):
+    """sa_bwd with the library's own scratch for the row terms: the caller
+    passes every output and nothing is allocated (see sa_bwd_noalloc in
+    sa.h: one earlier sa_bwd with the same layouts, B and H is needed)."""
+    import torch
+    B, H, n, d = q.shape
+    for name, t in (("q", q), ("k", k), ("v", v), ("o", o), ("do", do), ("dq", dq), ("dk", dk), ("dv", dv)):
+        _check_tensor(name, t, q.shape, q.dtype, q.device)
+    _check_tensor("lse", lse, (B, H, n), torch.float32, q.device)
+    heads = _head_array(layouts, H)
+    _check(_lib.sa_bwd_noalloc(heads, B, H, n, d, _dtype_code(q), float(scale), q.data_ptr(), k.data_ptr(),
+                               v.data_ptr(), o.data_ptr(), lse.data_ptr(), do.data_ptr(), dq.data_ptr(),
+                               dk.data_ptr(), dv.data_ptr(), _stream_handle(stream, q.device)))
     return dq, dk, dv
 
 

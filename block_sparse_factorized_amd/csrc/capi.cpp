@@ -411,8 +411,8 @@ namespace {
 // first and the dK/dV kernel after it (sa_bwd).
 enum BwdStage { kStageRowTerms = 1, kStageDkDv = 2, kStageDq = 4, kStageDqRowTerms = 8 };
 
-// alloc = false: the layouts and work lists must already be on the device;
-// nothing is allocated (a missing one is an error).
+// alloc = false (sa_bwd_noalloc): the layouts and work lists must already be
+// on the device; nothing is allocated (a missing one is an error).
 int bwd_call(const char* fn, int stages, const sa_layout_t* const* head_layout, int32_t B, int32_t H, int64_t n,
              int32_t d, int dtype, float scale, const void* q, const void* k, const void* v, const void* o,
              const float* lse, const void* dout, void* dq, void* dk, void* dv, void* workspace, size_t ws_bytes,
@@ -506,9 +506,52 @@ int bwd_call(const char* fn, int stages, const sa_layout_t* const* head_layout, 
     return SA_OK;
 }
 
+// Row-term scratch of sa_bwd_noalloc, one copy per device for the life of
+// the process: two fp32 per row, the layout sa_bwd's workspace has.
+constexpr size_t kScratchRows = (size_t)1 << 21;
+constexpr size_t kScratchBytes = 2 * kScratchRows * sizeof(float);  // 16 MiB
+static __device__ __align__(256) float scratch[2 * kScratchRows];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];  // device address of `scratch` per device (set on first use)
+
+// The device address of this device's scratch array.  The array's name is
+// a host-side stand-in, not a device address: kernels get this pointer.
+int scratch_on(int dev, void** out)
+{
+    if (dev < 0 || dev >= kMaxDevices) return fail(SA_ERR_UNSUPPORTED, "sa_bwd_noalloc: device %d beyond %d", dev, kMaxDevices);
+    std::lock_guard<std::mutex> g(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void* ptr = nullptr;
+        hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return hip_fail(e, "sa_bwd_noalloc: hipGetSymbolAddress(scratch)");
+        g_scratch_ptr[dev] = ptr;
+    }
+    *out = g_scratch_ptr[dev];
+    return SA_OK;
+}
+
 }  // namespace
 
 extern "C" {
+
+int sa_bwd_noalloc(const sa_layout_t* const* head_layout, int32_t B, int32_t H, int64_t n, int32_t d, int dtype,
+                   float scale, const void* q, const void* k, const void* v, const void* o, const float* lse,
+                   const void* dout, void* dq, void* dk, void* dv, void* stream)
+{
+    if (B >= 1 && H >= 1 && n >= 1 && (size_t)B * (size_t)H * (size_t)n > kScratchRows)
+        return fail(SA_ERR_INVALID_ARG, "sa_bwd_noalloc: B*H*n = %lld rows exceeds the scratch limit of %zu rows",
+                    (long long)B * H * n, kScratchRows);
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail(e, "sa_bwd_noalloc: hipGetDevice");
+    void* ws = nullptr;
+    int st = scratch_on(dev, &ws);
+    if (st != SA_OK) return st;
+    return bwd_call("sa_bwd_noalloc", kStageDqRowTerms | kStageDkDv, head_layout, B, H, n, d, dtype, scale, q, k, v,
+                    o, lse, dout, dq, dk, dv, ws, kScratchBytes, stream, false);
+}
 
 int sa_bwd(const sa_layout_t* const* head_layout, int32_t B, int32_t H, int64_t n, int32_t d, int dtype, float scale,
            const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dout, void* dq,

@@ -248,6 +248,27 @@ int sa_bwd(const sa_layout_t* const* head_layout, int32_t B, int32_t H, int64_t 
            size_t ws_bytes, void* stream);
 
 /*
+ * sa_bwd for callers that cannot allocate device memory: code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc.  The
+ * row terms go to a scratch array inside the library (one per device, held
+ * until the process ends) instead of a caller workspace; otherwise arguments,
+ * results and errors are sa_bwd's, and so are the kernels (bitwise the same
+ * gradients).  The call allocates nothing: the layouts and the work lists of
+ * (head_layout, B, H) must already be on the current device, which one
+ * earlier sa_bwd call with the same head_layout, B and H on that device
+ * ensures; else SA_ERR_UNSUPPORTED, launching nothing.  Limit: B*H*n <=
+ * 2^21 rows (16 MiB of scratch), else SA_ERR_INVALID_ARG.  Every call on a
+ * device shares that device's scratch: calls that overlap on one device (on
+ * different streams, or from several threads without ordering) race and
+ * give wrong gradients; calls ordered on one stream are safe.  The scratch
+ * needs no clearing (the first kernel writes every row term the second
+ * reads).
+ */
+int sa_bwd_noalloc(const sa_layout_t* const* head_layout, int32_t B, int32_t H, int64_t n, int32_t d,
+                   int dtype, float scale, const void* q, const void* k, const void* v, const void* o,
+                   const float* lse, const void* dout, void* dq, void* dk, void* dv, void* stream);
+
+/*
  * The stages of the backward pass as separate calls, for callers that
  * schedule them themselves.  Arguments mean what they mean for sa_bwd; each
  * call reads and writes only the pointers it takes.

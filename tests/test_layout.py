@@ -209,6 +209,11 @@ def test_fwd_bwd_argument_errors_without_gpu():
     st = lib.sa_fwd(hn, 1, 2, 256, 64, sa.SA_BF16, 1.0, p, p, p, p, p, None)
     assert st == sa.SA_ERR_INVALID_ARG
     assert sa.sa_bwd_workspace_size(2, 3, 100, 64) >= 2 * 3 * 100 * 4
+    # the allocation-free backward refuses more rows than its scratch holds
+    # (1 x 2 x 2^21 rows > 2^21) before any device work
+    big = sa.sa_layout_build("strided_a", 1 << 21, 1024, block=64)
+    st = lib.sa_bwd_noalloc(_heads(big, big), 1, 2, 1 << 21, 64, sa.SA_BF16, 1.0, p, p, p, p, p, p, p, p, p, None)
+    assert st == sa.SA_ERR_INVALID_ARG and b"scratch" in lib.sa_last_error()
 
 
 def test_residue_view_switch():
