@@ -85,6 +85,22 @@ def traffic_from_profile(kernel_file, kernel, workload):
     return None
 
 
+def counters_from_profile(kernel_file, kernel, workload):
+    """MFMA busy of a kernel from the rocprofv3 counter runs under profiles/
+    (counters.json), if they were taken on the current source of the
+    kernel's file (else None)."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", "counters.json")
+    src = os.path.join(ROOT, "block_sparse_factorized_amd", "csrc", kernel_file)
+    if not os.path.exists(path) or not os.path.exists(src):
+        return None
+    sha = hashlib.sha256(open(src, "rb").read()).hexdigest()
+    for e in json.load(open(path)).get("entries", []):
+        if e["kernel"] == kernel and e["workload"] == workload and e["source_sha256"] == sha:
+            return e
+    return None
+
+
 def measured_peaks():
     """The machine's own denominators (libsa_peaks.so, include/sa_peaks.h):
     the sustained bf16 MFMA rate of a kernel that does nothing else, and the
@@ -185,10 +201,27 @@ def live_quadrants(layouts, batch, T, raster_compact=False):
     return total * batch
 
 
-def cpu_baseline(w, x, pats, lays, T, max_heads):
+def _block_rel_l2(g, r):
+    """Largest relative L2 error over 64-row blocks, each against the larger
+    of its own norm and a tenth of the RMS block norm."""
+    import numpy as np
+    nb = max(1, -(-g.shape[0] // 64))
+    floor = 0.1 * np.linalg.norm(r) / np.sqrt(nb)
+    worst = 0.0
+    for a in range(0, g.shape[0], 64):
+        den = max(np.linalg.norm(r[a:a + 64]), floor, 1e-30)
+        worst = max(worst, float(np.linalg.norm(g[a:a + 64] - r[a:a + 64]) / den))
+    return worst
+
+
+def cpu_baseline(w, x, pats, lays, T, max_heads, outputs=None, runs=3):
     """The fp64 oracle on the host's cores over a bounded sample of heads of
     the same workload, fwd + bwd, scaled to the same counted-flop metric
-    (blocks counted as for the GPU run)."""
+    (blocks counted as for the GPU run); the median of `runs` timed passes.
+    The first pass's results are also compared with the GPU outputs of the
+    timed steps (`outputs`: host copies of o, lse and, with the backward,
+    dq, dk, dv), which gives the run's own parity figures."""
+    import numpy as np
     import oracle
     from workloads import to_f64
 
@@ -201,16 +234,43 @@ def cpu_baseline(w, x, pats, lays, T, max_heads):
     sample = sample[:max_heads]
     counted = 0.0
     elements = 0
-    t0 = time.perf_counter()
+    args = {bh: [to_f64(x[t][bh[0], bh[1]]) for t in (("q", "k", "v", "do") if w.backward else ("q", "k", "v"))]
+            for bh in sample}
     for (b, h) in sample:
-        p, l, c = pats[h]
-        args = [to_f64(x[t][b, h]) for t in ("q", "k", "v", "do")]
-        if w.backward:
-            oracle.head_bwd(p, l, c, *args, 1.0)
-        else:
-            oracle.head_fwd(p, l, c, *args[:3], 1.0)
         counted += listed_blocks(lays[h]) * 4.0 * T * T * w.d * (3.5 if w.backward else 1.0)
-    secs = time.perf_counter() - t0
+    times = []
+    err = {"o_max_abs": 0.0, "o_rel_l2": 0.0, "lse_max_abs": 0.0, "empty_rows_exact": True}
+    if w.backward:
+        err.update({"dq_rel_l2": 0.0, "dk_rel_l2": 0.0, "dv_rel_l2": 0.0, "grad_block_rel_l2": 0.0})
+    for run in range(runs):
+        t0 = time.perf_counter()
+        results = {}
+        for (b, h) in sample:
+            p, l, c = pats[h]
+            if w.backward:
+                results[(b, h)] = oracle.head_bwd(p, l, c, *args[(b, h)], 1.0)
+            else:
+                results[(b, h)] = (None, None, None) + tuple(oracle.head_fwd(p, l, c, *args[(b, h)], 1.0))
+        times.append(time.perf_counter() - t0)
+        if run > 0 or outputs is None:
+            continue
+        rel = lambda g, r: float(np.linalg.norm(g - r) / max(np.linalg.norm(r), 1e-30))
+        for (b, h), (rdq, rdk, rdv, ro, rlse) in results.items():
+            go = to_f64(outputs["o"][b, h])
+            glse = outputs["lse"][b, h].double().numpy()
+            fin = np.isfinite(rlse)
+            err["o_max_abs"] = max(err["o_max_abs"], float(np.abs(go - ro).max()))
+            err["o_rel_l2"] = max(err["o_rel_l2"], rel(go, ro))
+            if fin.any():
+                err["lse_max_abs"] = max(err["lse_max_abs"], float(np.abs(glse[fin] - rlse[fin]).max()))
+            err["empty_rows_exact"] = bool(err["empty_rows_exact"] and np.array_equal(np.isfinite(glse), fin)
+                                           and np.all(go[~fin] == 0.0))
+            if w.backward:
+                for nm, r in (("dq", rdq), ("dk", rdk), ("dv", rdv)):
+                    g = to_f64(outputs[nm][b, h])
+                    err[nm + "_rel_l2"] = max(err[nm + "_rel_l2"], rel(g, r))
+                    err["grad_block_rel_l2"] = max(err["grad_block_rel_l2"], _block_rel_l2(g, r))
+    secs = float(np.median(times))
     for (b, h) in sample:
         p, l, c = pats[h]
         elements += int(oracle.row_counts(p, w.n, l, c).sum())
@@ -220,17 +280,28 @@ def cpu_baseline(w, x, pats, lays, T, max_heads):
             cpu_model = next((ln.split(":", 1)[1].strip() for ln in f if ln.startswith("model name")), None)
     except OSError:
         pass
+    parity = None
+    if outputs is not None:
+        # the acceptance bars: O max-abs 2e-2 (bf16) or 1e-4 (fp32), gradients 5e-2 relative L2
+        o_bar = 2e-2 if w.dtype == "bf16" else 1e-4
+        ok = err["o_max_abs"] <= o_bar and err["empty_rows_exact"]
+        if w.backward:
+            ok = ok and max(err["dq_rel_l2"], err["dk_rel_l2"], err["dv_rel_l2"]) <= 5e-2
+        parity = dict(err, heads=len(sample), o_max_abs_bar=o_bar, grad_rel_l2_bar=5e-2 if w.backward else None,
+                      passed=bool(ok), against="the fp64 oracle on the timed steps' outputs, whole heads")
     return {
         "value": counted / secs / 1e12,
         "unit": "TFLOP/s",
         "cores": oracle.num_threads(),
         "kind": "oracle",
-        "sample": "%d of %d heads of %s (b,h in A/B pairs), fwd%s in fp64, %.1f s"
-                  % (len(sample), w.batch * w.heads, w.name, "+bwd" if w.backward else "", secs),
+        "sample": "%d of %d heads of %s (b,h in A/B pairs), fwd%s in fp64, median of %d passes of %.1f s"
+                  % (len(sample), w.batch * w.heads, w.name, "+bwd" if w.backward else "", runs, secs),
         "seconds": secs,
+        "seconds_each": times,
         "cpu_model": cpu_model,
         # the oracle's own work: 4 d flops per allowed element forward, 10 d backward
         "allowed_element_gflops": elements * w.d * (14.0 if w.backward else 4.0) / secs / 1e9,
+        "parity": parity,
     }
 
 
@@ -475,6 +546,7 @@ def main():
     # Allowed (query, key) pairs over the elements of the walked blocks.
     allowed = sum(lay.info()["allowed"] for lay in lays) * w.batch
     traffic = traffic_from_profile(kern_file, kern_sym[dominant], label)
+    ctr = counters_from_profile(kern_file, kern_sym[dominant], label)
     roofline = {
         "kernel": kern_sym[dominant],
         "bound": "mfma",
@@ -490,6 +562,11 @@ def main():
         # What the matrix cores actually execute (empty quadrants skipped).
         "executed_mfma_tflops": dk_["executed_tflops"],
         "executed_frac": dk_["executed_tflops"] / peak,
+        # rocprofv3 counters of the same kernel and workload (profiles/mfma_busy.md):
+        # SQ_VALU_MFMA_BUSY_CYCLES over the XCD's GPU-busy cycles times 1024 SIMDs,
+        # and over the traced duration at 2.4 GHz; null once the source changed
+        "mfma_busy": ctr["mfma_busy_grbm"] if ctr else None,
+        "mfma_busy_at_2400mhz": ctr["mfma_busy_at_2400mhz"] if ctr else None,
         "frac_of_measured_peak": dk_["tflops"] / mpeak if mpeak else None,
     }
     out = {
@@ -517,6 +594,9 @@ def main():
         "measured_peaks": mp,
         "frac_of_measured_peak": value / mpeak if mpeak else None,
         "useful_element_fraction": allowed / (blocks * T * T) if blocks else None,
+        # the pattern's own work: 4 d flops per allowed (query, key) pair
+        # forward and 10 d backward, over the step time
+        "useful_pair_tflops": allowed * w.d * (14.0 if w.backward else 4.0) / (ms_per_step * 1e-3) / 1e12,
         # With a residue or compact view, the raster layouts' block count over
         # the same step time (a reference only: the views walk fewer blocks).
         "raster_counted_tflops": (sum(lay.info()["nnz"] for lay in lays) * w.batch * 4.0 * T * T * d
@@ -529,10 +609,16 @@ def main():
         "layout_build_ms": layout_ms,
         "roofline": roofline,
         "cpu_baseline": None,
+        "parity": None,
     }
     if not args.no_cpu_baseline:
         heads = args.cpu_heads or {"tiny": 2, "img32": 16, "text": 16, "img64": 32, "audio": 2}[w.name]
-        out["cpu_baseline"] = cpu_baseline(w, x, pats, lays, T, heads)
+        outs = {"o": o.cpu(), "lse": lse.cpu()}
+        if w.backward:
+            outs.update(dq=dq.cpu(), dk=dk.cpu(), dv=dv.cpu())
+        out["cpu_baseline"] = cpu_baseline(w, x, pats, lays, T, heads, outputs=outs)
+        # the same run's correctness figures, next to the rate they qualify
+        out["parity"] = out["cpu_baseline"].pop("parity")
     print(json.dumps(out), flush=True)
 
 
