@@ -134,6 +134,8 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(const BwdArgs a)
     const float* dlg = a.ndelta + lrow0;
     const int k_local = 32 * kh + n32;
     const int k_row = (kb < 0 ? 0 : kb) * T + k_local;
+    // this wave holds keys that are not padding of a ragged last block
+    const bool keys_live = kb >= 0 && kb * T + 32 * kh < vm;
 
     bf16x8 kop[D / 16], vop[D / 16];
     {
@@ -217,7 +219,7 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(const BwdArgs a)
         st_cur = st_nxt;
         st_nxt = ld_uniform(&L.kgrp_step[p0 + min(t + 2, nblk - 1)]);
         const int mid = member ? step.z : step.y;  // -2: this key block is not listed
-        if (kb >= 0 && mid != -2) {
+        if (keys_live && mid != -2) {
             // Transposed lane-mask planes (set 0, all ones, for a full block).
             // A 32-query half is live when the mask has an allowed element in
             // quadrant (query half qt, key half kh).
@@ -426,6 +428,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D == 64 ? 4
     const int q_local = 32 * wr + n32;
     const int q_row = (qb < 0 ? 0 : qb) * T + q_local;
     const int q_rc = min(q_row, vm - 1);  // clamped for reads
+    // this wave has rows that are not padding of a ragged last block
+    const bool rows_live = qb >= 0 && qb * T + 32 * wr < vm;
 
     bf16x8 qop[D / 16], dop[D / 16];
     {
@@ -521,7 +525,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D == 64 ? 4
         st_cur = st_nxt;
         st_nxt = ld_uniform(&L.qgrp_step[p0 + min(t + 2, nblk - 1)]);
         const int mid = member ? step.z : step.y;  // -2: not in this block's list
-        if (qb >= 0 && mid != -2) {
+        if (rows_live && mid != -2) {
             // Lane-mask planes (set 0, all ones, for a full block) first, so the
             // scalar loads overlap the products.  A 32-key half is live when
             // the mask has an allowed element in quadrant (query half wr, key

@@ -95,6 +95,8 @@ __global__ __launch_bounds__(256) void fwd_bf16_t64_kernel(const FwdArgs a)
     const unsigned short* V = (const unsigned short*)a.v + head;
     const int q_local = 32 * wr + n32;
     const int q_row = (qb < 0 ? 0 : qb) * T + q_local;
+    // this wave has rows that are not padding of a ragged last block
+    const bool rows_live = qb >= 0 && qb * T + 32 * wr < vm;
 
     // Q^T as the B operand of S^T = K Q^T: lane (hh, n) holds d = 16c + 8hh .. +7 of query n.
     bf16x8 qop[D / 16];
@@ -173,7 +175,7 @@ __global__ __launch_bounds__(256) void fwd_bf16_t64_kernel(const FwdArgs a)
         st_cur = st_nxt;
         st_nxt = ld_uniform(&L.qgrp_step[p0 + min(t + 2, nblk - 1)]);
         const int mid = member ? step.z : step.y;  // -2: not in this block's list
-        if (qb >= 0 && mid != -2) {
+        if (rows_live && mid != -2) {
             // Lane masks of every score register, one 64-bit plane each (a full
             // block reads plane set 0, all ones); the constant address space makes
             // these wave-uniform loads scalar loads.
