@@ -108,6 +108,10 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(const BwdArgs a)
     const int n32 = lane & 31, hh = lane >> 5;
     const Item item = ld_uniform(&a.items[blockIdx.x]);
     const int bh = item.bh, grp = item.blk;
+    // A chunk of a compact view's query list: steps item.r .. +chunk_steps-1,
+    // summed into partial-sum slot item.slot (no residue class).
+    const bool chunk = item.slot >= 0;
+    const int res = chunk ? 0 : item.r;
     const DevLayout L = a.heads.lay[a.heads.head_lay[bh % a.H]];
     const int2 pair = ld_uniform(&L.kgrp_blk[grp]);
     const int kb = member ? pair.y : pair.x;  // -1: this wave has no keys
@@ -122,12 +126,12 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(const BwdArgs a)
     const unsigned qsel = kmode ? 1u << wr : 3u;
     // The walked sequence: row m is position r + vl*m of the head (vl = 1,
     // r = 0 for a plain layout), rs elements apart; rows >= vm are read
-    // clamped, get zero weight and are never written.  (Never a compact
-    // view: its key rows are not remapped here.)
-    const int vl = L.vl, vm = L.vm;
+    // clamped, get zero weight and are never written.  Key t is row
+    // key_pos(t) of it (the compact view's summary keys), km keys valid.
+    const int vl = L.vl, vm = L.vm, km = L.km;
     const int rs = vl * D;
-    const int64_t head = (int64_t)bh * a.n * D + (int64_t)item.r * D;
-    const int64_t lrow0 = (int64_t)bh * a.n + item.r;  // row-term index of row 0
+    const int64_t head = (int64_t)bh * a.n * D + (int64_t)res * D;
+    const int64_t lrow0 = (int64_t)bh * a.n + res;  // row-term index of row 0
     const unsigned short* Q = (const unsigned short*)a.q + head;
     const unsigned short* dO = (const unsigned short*)a.dout + head;
     const float* nl2g = a.nl2 + lrow0;
@@ -135,11 +139,11 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(const BwdArgs a)
     const int k_local = 32 * kh + n32;
     const int k_row = (kb < 0 ? 0 : kb) * T + k_local;
     // this wave holds keys that are not padding of a ragged last block
-    const bool keys_live = kb >= 0 && kb * T + 32 * kh < vm;
+    const bool keys_live = kb >= 0 && kb * T + 32 * kh < km;
 
     bf16x8 kop[D / 16], vop[D / 16];
     {
-        const uint32_t kr = (uint32_t)(min(k_row, vm - 1) * rs);
+        const uint32_t kr = (uint32_t)(key_pos(L, min(k_row, km - 1)) * rs);
         const unsigned short* K = (const unsigned short*)a.k + head + kr;
         const unsigned short* V = (const unsigned short*)a.v + head + kr;
 #pragma unroll
@@ -169,8 +173,10 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(const BwdArgs a)
         zero(dk[dt]);
         zero(dv[dt]);
     }
-    const int p0 = ld_uniform(&L.kgrp_ptr[grp]);
-    const int nblk = ld_uniform(&L.kgrp_ptr[grp + 1]) - p0;
+    const int g0 = ld_uniform(&L.kgrp_ptr[grp]);
+    const int glen = ld_uniform(&L.kgrp_ptr[grp + 1]) - g0;
+    const int p0 = chunk ? g0 + item.r : g0;
+    const int nblk = chunk ? min(a.chunk_steps, glen - item.r) : glen;
     const float c2 = a.scale_log2;
 
     // Starts the loads of query tile qb into (qd, od) and returns this lane's
@@ -351,15 +357,31 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(const BwdArgs a)
     // Each wave writes one 32-key half of its block (its valid rows).  In a shared-half member
     // wave 0 writes the shared half, wave 1 the other half, whose keys no
     // query reaches: zeros.
-    int out_row = k_row;
+    int out_local = k_local;
     if (kmode && wr == 1) {
-        out_row = kb * T + 32 * (1 - kh) + n32;
+        out_local = 32 * (1 - kh) + n32;
 #pragma unroll
         for (int dt = 0; dt < D / 32; ++dt) {
             zero(dk[dt]);
             zero(dv[dt]);
         }
     }
+    if (chunk) {
+        // The chunk's fp32 partial sums (dK unscaled), [dK, dV][member][key][d]:
+        // the summing pass adds the chunks of each pair in order.
+        float* P = a.partials + (int64_t)item.slot * kSlotFloats(D) + (int64_t)(member * 64 + out_local) * D;
+        float* PV = P + 2 * 64 * D;
+#pragma unroll
+        for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const int c = 32 * dt + 8 * g + 4 * hh;
+                *(f32x4*)(P + c) = f32x4{dk[dt][4 * g], dk[dt][4 * g + 1], dk[dt][4 * g + 2], dk[dt][4 * g + 3]};
+                *(f32x4*)(PV + c) = f32x4{dv[dt][4 * g], dv[dt][4 * g + 1], dv[dt][4 * g + 2], dv[dt][4 * g + 3]};
+            }
+        return;
+    }
+    const int out_row = kb * T + out_local;
     if (out_row >= vm) return;  // a ragged block's padding row
     // Register i of dk[dt]/dv[dt]: d = 32*dt + 8*(i/4) + 4*hh + i%4 of key out_row.
     unsigned short* DK = (unsigned short*)a.dk + head + (uint32_t)(out_row * rs);
@@ -376,6 +398,61 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(const BwdArgs a)
             *(u32x2*)(DK + 32 * dt + 8 * g + 4 * hh) = uk;
             *(u32x2*)(DV + 32 * dt + 8 * g + 4 * hh) = uv;
         }
+}
+
+// ---------------------------------------------------------------------------
+// Summing pass of a compact view's dK/dV (fixed B): the dK/dV kernel walks
+// each key-block pair of summary keys in chunks of its query list and leaves
+// one fp32 partial sum per chunk; here every row of the head is written
+// once: a summary row (position j with j mod l >= l - c, key t = (j / l) c +
+// j mod l - (l - c)) gets the sum of its pair's chunks taken in chunk order,
+// dK scaled, both rounded to bf16; every other row, which no query
+// reaches, gets zeros.  One workgroup per 64 rows of one head, D/8 threads
+// per row, 8 consecutive elements each.
+template <int D>
+__global__ __launch_bounds__(256) void bwd_dkdv_reduce_kernel(const ReduceArgs a)
+{
+    constexpr int TPR = D / 8, RPP = 256 / TPR;  // threads per row, rows per pass
+    const int64_t nrb = (a.n + 63) / 64;
+    const int hx = (int)(blockIdx.x / nrb);
+    const int64_t r0 = (int64_t)(blockIdx.x % nrb) * 64;
+    const int2 ht = ld_uniform(&a.heads_tab[hx]);  // {bh, offset into groups}
+    const DevLayout L = a.heads.lay[a.heads.head_lay[ht.x % a.H]];
+    const int l = L.kgl, c = 1 << L.kcl, off = L.koff;
+    const int part = threadIdx.x % TPR;
+    for (int pass = 0; pass < 64 / RPP; ++pass) {
+        const int64_t j = r0 + pass * RPP + threadIdx.x / TPR;
+        if (j >= a.n) break;
+        f32x4 k0 = {0.f, 0.f, 0.f, 0.f}, k1 = k0, v0 = k0, v1 = k0;
+        const int jm = (int)(j % l);
+        if (jm >= off) {
+            const int t = (int)(j / l) * c + (jm - off);
+            const int2 gm = L.kblk_grp[t >> 6];  // {pair, member}
+            if (gm.x >= 0) {
+                const int2 gs = a.groups[ht.y + gm.x];  // {first slot, chunks}
+                const int64_t e = (int64_t)(gm.y * 64 + (t & 63)) * D + 8 * part;
+                for (int ch = 0; ch < gs.y; ++ch) {
+                    const float* P = a.partials + (int64_t)(gs.x + ch) * kSlotFloats(D) + e;
+                    k0 += *(const f32x4*)P;
+                    k1 += *(const f32x4*)(P + 4);
+                    v0 += *(const f32x4*)(P + 2 * 64 * D);
+                    v1 += *(const f32x4*)(P + 2 * 64 * D + 4);
+                }
+            }
+        }
+        const int64_t o = ((int64_t)ht.x * a.n + j) * D + 8 * part;
+        u32x4 uk, uv;
+        uk[0] = bf16_pair(k0[0] * a.scale, k0[1] * a.scale);
+        uk[1] = bf16_pair(k0[2] * a.scale, k0[3] * a.scale);
+        uk[2] = bf16_pair(k1[0] * a.scale, k1[1] * a.scale);
+        uk[3] = bf16_pair(k1[2] * a.scale, k1[3] * a.scale);
+        uv[0] = bf16_pair(v0[0], v0[1]);
+        uv[1] = bf16_pair(v0[2], v0[3]);
+        uv[2] = bf16_pair(v1[0], v1[1]);
+        uv[3] = bf16_pair(v1[2], v1[3]);
+        *(u32x4*)((unsigned short*)a.dk + o) = uk;
+        *(u32x4*)((unsigned short*)a.dv + o) = uv;
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -670,6 +747,16 @@ hipError_t launch_bwd_dkdv_bf16_t64(int d, const BwdArgs& a, int n_items, hipStr
         hipLaunchKernelGGL(bwd_dkdv_kernel<64>, dim3(n_items), dim3(256), 0, stream, a);
     else
         hipLaunchKernelGGL(bwd_dkdv_kernel<128>, dim3(n_items), dim3(256), 0, stream, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_bwd_dkdv_reduce_bf16(int d, const ReduceArgs& a, int n_heads, int64_t n, hipStream_t stream)
+{
+    const dim3 g((unsigned)(n_heads * ((n + 63) / 64))), b(256);
+    if (d == 64)
+        hipLaunchKernelGGL(bwd_dkdv_reduce_kernel<64>, g, b, 0, stream, a);
+    else
+        hipLaunchKernelGGL(bwd_dkdv_reduce_kernel<128>, g, b, 0, stream, a);
     return hipGetLastError();
 }
 

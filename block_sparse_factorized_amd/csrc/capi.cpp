@@ -67,10 +67,25 @@ int device_layout(sa_layout* L, int dev, DevLayout* out, bool upload)
 // Work lists (build_work_items), uploaded once and cached per (kind, device,
 // B, H, layouts).
 
+// Steps per chunk of a compact view's query list in the dK/dV kernel: long
+// enough to amortise a chunk's partial sums, short enough that the first
+// key-block pairs (listed by nearly every query block) do not set the
+// launch time.  Measured on text (n = 12288, l = 128, c = 32, lists of up to
+// 192 steps): dK/dV with its summing pass 232 us at 64 steps, 217 at 96,
+// 233 at 128, 293 unsplit, against 226 on the raster layout.
+constexpr int32_t kChunkSteps = 96;
+
 struct Plan {
     Item* items;
     int count;
     int dev;
+    void* mem;  // the one allocation behind everything below
+    // dK/dV of compact views (kByKeyPair only): the summing pass's tables
+    // (see ReduceArgs) and the chunks' partial sums.
+    const int2* rheads;
+    int n_rheads;
+    const int2* rgroups;
+    float* partials;
 };
 
 std::mutex g_plan_mu;
@@ -81,9 +96,9 @@ std::map<std::string, Plan, std::less<>> g_plans;  // looked up by string_view: 
 std::map<uint64_t, std::vector<std::string>> g_plan_keys;
 
 // The cache key of a work list, written into buf (no allocation); returns its length.
-size_t plan_key(char* buf, size_t cap, ListKind kind, int dev, int32_t B, int32_t H, sa_layout* const* hl)
+size_t plan_key(char* buf, size_t cap, ListKind kind, int dev, int32_t B, int32_t H, int32_t d, sa_layout* const* hl)
 {
-    size_t len = (size_t)snprintf(buf, cap, "%d:%d:%d:%d", (int)kind, dev, B, H);
+    size_t len = (size_t)snprintf(buf, cap, "%d:%d:%d:%d:%d", (int)kind, dev, B, H, d);
     for (int32_t h = 0; h < H && len < cap; ++h)
         len += (size_t)snprintf(buf + len, cap - len, ":%llu", (unsigned long long)hl[h]->serial);
     return std::min(len, cap - 1);
@@ -91,10 +106,10 @@ size_t plan_key(char* buf, size_t cap, ListKind kind, int dev, int32_t B, int32_
 
 // The work list of a call, built and uploaded on first use.  create = false:
 // only look it up (no allocation); SA_ERR_UNSUPPORTED when it is not cached.
-int get_plan(ListKind kind, int dev, int32_t B, int32_t H, sa_layout* const* hl, Plan* out, bool create)
+int get_plan(ListKind kind, int dev, int32_t B, int32_t H, int32_t d, sa_layout* const* hl, Plan* out, bool create)
 {
-    char kbuf[32 + 21 * kMaxHeads];  // "kind:dev:B:H" + ":serial" per head
-    const size_t klen = plan_key(kbuf, sizeof kbuf, kind, dev, B, H, hl);
+    char kbuf[48 + 21 * kMaxHeads];  // "kind:dev:B:H:d" + ":serial" per head
+    const size_t klen = plan_key(kbuf, sizeof kbuf, kind, dev, B, H, d, hl);
     std::lock_guard<std::mutex> g(g_plan_mu);
     auto it = g_plans.find(std::string_view(kbuf, klen));
     if (it != g_plans.end()) {
@@ -106,17 +121,32 @@ int get_plan(ListKind kind, int dev, int32_t B, int32_t H, sa_layout* const* hl,
                     "sa_bwd with the same arguments caches it)", dev);
     const std::string key(kbuf, klen);
     std::vector<Item> sorted;
-    build_work_items(kind, B, H, hl, &sorted);
+    DkdvSplit split;
+    build_work_items(kind, B, H, hl, kind == kByKeyPair ? kChunkSteps : 0, &sorted, &split);
     const int64_t count = (int64_t)sorted.size();
+    // One allocation: items, then (dK/dV of compact views) the summing
+    // pass's tables and the partial sums, each 256-byte aligned.
+    auto al = [](size_t x) { return (x + 255) & ~(size_t)255; };
+    const size_t off_heads = al(sorted.size() * sizeof(Item));
+    const size_t off_groups = al(off_heads + split.heads.size() * sizeof(int2));
+    const size_t off_part = al(off_groups + split.groups.size() * sizeof(int2));
+    const size_t total = off_part + (size_t)split.slots * (size_t)kSlotFloats(d) * sizeof(float);
+    std::vector<unsigned char> host(off_part, 0);
+    if (!sorted.empty()) memcpy(host.data(), sorted.data(), sorted.size() * sizeof(Item));
+    if (!split.heads.empty()) memcpy(host.data() + off_heads, split.heads.data(), split.heads.size() * sizeof(int2));
+    if (!split.groups.empty())
+        memcpy(host.data() + off_groups, split.groups.data(), split.groups.size() * sizeof(int2));
     void* mem = nullptr;
-    hipError_t e = hipMalloc(&mem, sorted.size() * sizeof(Item));
-    if (e != hipSuccess) return fail(SA_ERR_ALLOC, "work list: hipMalloc: %s", hipGetErrorString(e));
-    e = hipMemcpy(mem, sorted.data(), sorted.size() * sizeof(Item), hipMemcpyHostToDevice);
+    hipError_t e = hipMalloc(&mem, std::max<size_t>(total, 256));
+    if (e != hipSuccess) return fail(SA_ERR_ALLOC, "work list: hipMalloc(%zu): %s", total, hipGetErrorString(e));
+    e = hipMemcpy(mem, host.data(), off_part, hipMemcpyHostToDevice);
     if (e != hipSuccess) {
         (void)hipFree(mem);
         return hip_fail(e, "work list: hipMemcpy");
     }
-    Plan p{(Item*)mem, (int)count, dev};
+    unsigned char* base = (unsigned char*)mem;
+    Plan p{(Item*)mem, (int)count, dev, mem, (const int2*)(base + off_heads), (int)split.heads.size(),
+           (const int2*)(base + off_groups), split.slots ? (float*)(base + off_part) : nullptr};
     g_plans[key] = p;
     for (int32_t h = 0; h < H; ++h) {
         std::vector<std::string>& keys = g_plan_keys[hl[h]->serial];
@@ -137,7 +167,7 @@ void release_plans(uint64_t serial)
         if (p == g_plans.end()) continue;
         int cur = 0;
         if (hipGetDevice(&cur) == hipSuccess && hipSetDevice(p->second.dev) == hipSuccess) {
-            (void)hipFree(p->second.items);
+            (void)hipFree(p->second.mem);
             (void)hipSetDevice(cur);
         }
         g_plans.erase(p);
@@ -147,14 +177,10 @@ void release_plans(uint64_t serial)
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15) == 0; }
 
-// Checks shared by sa_fwd and sa_bwd; fills the head table.
-// compact: walk compact views (the forward and dQ kernels); the dK/dV
-// kernel walks those layouts in their raster form, whose key blocks have
-// more and shorter query lists (the compact view's first key blocks are
-// listed by almost every query block, and a few long workgroups would set
-// the launch time).
+// Checks shared by sa_fwd and sa_bwd; fills the head table with the layouts
+// the kernels walk (a layout's view when it has one).
 int common_checks(const char* fn, const sa_layout_t* const* head_layout, int32_t B, int32_t H, int64_t n,
-                  int32_t d, int dtype, float scale, bool backward, bool compact, HeadTable* ht,
+                  int32_t d, int dtype, float scale, bool backward, HeadTable* ht,
                   sa_layout** hl /* [kMaxHeads] */, sa_layout** distinct_out, int* n_distinct)
 {
     if (!head_layout) return fail(SA_ERR_INVALID_ARG, "%s: head_layout is NULL", fn);
@@ -184,7 +210,7 @@ int common_checks(const char* fn, const sa_layout_t* const* head_layout, int32_t
         if (L->T != block)
             return fail(SA_ERR_UNSUPPORTED, "%s: head_layout[%d] has block %d; %s kernels need block %d", fn, h, L->T,
                         dtype == SA_F32 ? "f32" : "bf16", block);
-        if (L->view && (compact || L->view_kind != 2)) L = L->view;  // the kernels walk the view
+        if (L->view) L = L->view;  // the kernels walk the view
         int idx = -1;
         for (int a = 0; a < nl; ++a)
             if (distinct[a] == L) idx = a;
@@ -355,7 +381,7 @@ int sa_fwd(const sa_layout_t* const* head_layout, int32_t B, int32_t H, int64_t 
     int dev = 0, nl = 0;
     sa_layout* hl[kMaxHeads];
     sa_layout* distinct[kMaxLayouts];
-    int st = common_checks("sa_fwd", head_layout, B, H, n, d, dtype, scale, false, true, &ht, hl, distinct, &nl);
+    int st = common_checks("sa_fwd", head_layout, B, H, n, d, dtype, scale, false, &ht, hl, distinct, &nl);
     if (st != SA_OK) return st;
     if (!q || !k || !v || !o || !lse) return fail(SA_ERR_INVALID_ARG, "sa_fwd: NULL tensor pointer");
     if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || ((uintptr_t)lse & 3))
@@ -363,7 +389,7 @@ int sa_fwd(const sa_layout_t* const* head_layout, int32_t B, int32_t H, int64_t 
     st = prepare_device(distinct, nl, &ht, &dev, true);
     if (st != SA_OK) return st;
     Plan plan;
-    st = get_plan(dtype == SA_BF16 ? kByQueryPair : kByQuery, dev, B, H, hl, &plan, true);
+    st = get_plan(dtype == SA_BF16 ? kByQueryPair : kByQuery, dev, B, H, d, hl, &plan, true);
     if (st != SA_OK) return st;
     FwdArgs a;
     a.q = q;
@@ -418,15 +444,11 @@ int bwd_call(const char* fn, int stages, const sa_layout_t* const* head_layout, 
              const float* lse, const void* dout, void* dq, void* dk, void* dv, void* workspace, size_t ws_bytes,
              void* stream, bool alloc = true)
 {
-    HeadTable ht, htk;  // htk: for the dK/dV kernel (no compact views)
-    int dev = 0, nl = 0, nlk = 0;
+    HeadTable ht;
+    int dev = 0, nl = 0;
     sa_layout* hl[kMaxHeads];
-    sa_layout* hlk[kMaxHeads];
     sa_layout* distinct[kMaxLayouts];
-    sa_layout* distinct_k[kMaxLayouts];
-    int st = common_checks(fn, head_layout, B, H, n, d, dtype, scale, true, true, &ht, hl, distinct, &nl);
-    if (st != SA_OK) return st;
-    st = common_checks(fn, head_layout, B, H, n, d, dtype, scale, true, false, &htk, hlk, distinct_k, &nlk);
+    int st = common_checks(fn, head_layout, B, H, n, d, dtype, scale, true, &ht, hl, distinct, &nl);
     if (st != SA_OK) return st;
     // Pointers each stage reads or writes.
     const bool rt = stages & kStageRowTerms, kv = stages & kStageDkDv, dqs = stages & (kStageDq | kStageDqRowTerms);
@@ -445,15 +467,13 @@ int bwd_call(const char* fn, int stages, const sa_layout_t* const* head_layout, 
                     sa_bwd_workspace_size(B, H, n, d));
     st = prepare_device(distinct, nl, &ht, &dev, alloc);
     if (st != SA_OK) return st;
-    st = prepare_device(distinct_k, nlk, &htk, &dev, alloc);
-    if (st != SA_OK) return st;
-    Plan pk{nullptr, 0}, pq{nullptr, 0};
+    Plan pk{}, pq{};
     if (kv) {
-        st = get_plan(kByKeyPair, dev, B, H, hlk, &pk, alloc);
+        st = get_plan(kByKeyPair, dev, B, H, d, hl, &pk, alloc);
         if (st != SA_OK) return st;
     }
     if (dqs) {
-        st = get_plan(kByQueryPair, dev, B, H, hl, &pq, alloc);
+        st = get_plan(kByQueryPair, dev, B, H, d, hl, &pq, alloc);
         if (st != SA_OK) return st;
     }
     BwdArgs a;
@@ -475,6 +495,8 @@ int bwd_call(const char* fn, int stages, const sa_layout_t* const* head_layout, 
     a.scale_log2 = scale * 1.4426950408889634f;
     a.heads = ht;
     a.items = nullptr;
+    a.partials = pk.partials;
+    a.chunk_steps = kChunkSteps;
     hipStream_t s = (hipStream_t)stream;
     hipError_t e;
     // The dQ kernel's one-element form pays off where such quadrants occur
@@ -493,9 +515,24 @@ int bwd_call(const char* fn, int stages, const sa_layout_t* const* head_layout, 
     }
     if (kv) {
         a.items = pk.items;
-        a.heads = htk;
+        a.heads = ht;
         e = launch_bwd_dkdv_bf16_t64(d, a, pk.count, s);
         if (e != hipSuccess) return hip_fail(e, "sa_bwd: dK/dV kernel launch");
+        if (pk.n_rheads > 0) {
+            // compact views: sum each key-block pair's chunks in order
+            ReduceArgs r;
+            r.dk = dk;
+            r.dv = dv;
+            r.partials = pk.partials;
+            r.heads_tab = pk.rheads;
+            r.groups = pk.rgroups;
+            r.n = n;
+            r.H = H;
+            r.scale = scale;
+            r.heads = ht;
+            e = launch_bwd_dkdv_reduce_bf16(d, r, pk.n_rheads, n, s);
+            if (e != hipSuccess) return hip_fail(e, "sa_bwd: dK/dV summing launch");
+        }
     }
     if (dqs && !dq_rt) {
         a.items = pq.items;

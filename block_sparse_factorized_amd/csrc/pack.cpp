@@ -42,6 +42,9 @@ int pack_layout(sa_layout* L, LayoutImage* img)
     const size_t n_kgroups = L->kgroups.ptr.empty() ? 0 : L->kgroups.ptr.size() - 1;
     const size_t off_kmode = cur;
     cur = al(off_kmode + n_kgroups * 4);
+    // Per key block: its pair and member.
+    const size_t off_kblk = cur;
+    cur = al(off_kblk + (size_t)L->nkb * 8);
     size_t total = cur;
     std::vector<unsigned char> host(total, 0);
     if (nwords) {
@@ -173,6 +176,19 @@ int pack_layout(sa_layout* L, LayoutImage* img)
             }
             km[g] = mode;
         }
+        int32_t* kg = (int32_t*)&host[off_kblk];
+        for (int64_t b = 0; b < L->nkb; ++b) {
+            kg[2 * b] = -1;
+            kg[2 * b + 1] = 0;
+        }
+        for (size_t g = 0; g < n_kgroups; ++g)
+            for (int m = 0; m < 2; ++m) {
+                const int32_t b = L->kgroups.blk[2 * g + m];
+                if (b >= 0 && b < L->nkb) {
+                    kg[2 * b] = (int32_t)g;
+                    kg[2 * b + 1] = m;
+                }
+            }
     }
     img->host = std::move(host);
     img->has_planes = nplanes != 0;
@@ -187,6 +203,7 @@ int pack_layout(sa_layout* L, LayoutImage* img)
     img->off_row_idx = off_row_idx;
     img->off_col_mask = off_col_mask;
     img->off_kmode = off_kmode;
+    img->off_kblk = off_kblk;
     for (int k = 0; k < 2; ++k) {
         img->off_gptr[k] = off_gptr[k];
         img->off_gblk[k] = off_gblk[k];
@@ -215,6 +232,7 @@ DevLayout place_layout(const LayoutImage& img, const sa_layout* L, const unsigne
     v.kgrp_blk = (const int2*)(b + img.off_gblk[1]);
     v.kgrp_step = (const int4*)(b + img.off_gstep[1]);
     v.kgrp_mode = (const int32_t*)(b + img.off_kmode);
+    v.kblk_grp = (const int2*)(b + img.off_kblk);
     v.vl = (int32_t)L->view_l;
     v.vm = (int32_t)L->view_m;
     v.kcl = L->key_cl;
@@ -224,7 +242,8 @@ DevLayout place_layout(const LayoutImage& img, const sa_layout* L, const unsigne
     return v;
 }
 
-void build_work_items(ListKind kind, int32_t B, int32_t H, sa_layout* const* hl, std::vector<Item>* out)
+void build_work_items(ListKind kind, int32_t B, int32_t H, sa_layout* const* hl, int32_t chunk_steps,
+                      std::vector<Item>* out, DkdvSplit* split)
 {
     auto listing = [&](const sa_layout* L) -> const std::vector<int32_t>& {
         switch (kind) {
@@ -233,27 +252,44 @@ void build_work_items(ListKind kind, int32_t B, int32_t H, sa_layout* const* hl,
         default: return L->kgroups.ptr;
         }
     };
-    // (a residue view walks its dense causal layout once per residue class)
-    int64_t count = 0;
-    for (int32_t bh = 0; bh < B * H; ++bh)
-        count += ((int64_t)listing(hl[bh % H]).size() - 1) * hl[bh % H]->view_l;
-    std::vector<Item> items((size_t)count);
-    std::vector<int32_t> cost((size_t)count);
-    size_t x = 0;
+    // A compact view's key-block pairs are walked in chunks of at most
+    // chunk_steps steps, each with a partial-sum slot, by the dK/dV kernel.
+    const bool chunked = kind == kByKeyPair && chunk_steps > 0;
+    if (split) *split = DkdvSplit();
+    std::vector<Item> items;
+    std::vector<int32_t> cost;
     for (int32_t bh = 0; bh < B * H; ++bh) {
         const sa_layout* L = hl[bh % H];
         const std::vector<int32_t>& ptr = listing(L);
+        if (chunked && is_compact(L)) {
+            if (split) split->heads.push_back(make_int2(bh, (int32_t)split->groups.size()));
+            for (int64_t blk = 0; blk + 1 < (int64_t)ptr.size(); ++blk) {
+                const int32_t len = ptr[blk + 1] - ptr[blk];
+                const int32_t chunks = std::max<int32_t>(1, (len + chunk_steps - 1) / chunk_steps);
+                const int32_t first = split ? (int32_t)split->slots : 0;
+                for (int32_t c = 0; c < chunks; ++c) {
+                    items.push_back(Item{bh, (int32_t)blk, c * chunk_steps, first + c});
+                    cost.push_back(std::min(chunk_steps, len - c * chunk_steps));
+                }
+                if (split) {
+                    split->groups.push_back(make_int2(first, chunks));
+                    split->slots += chunks;
+                }
+            }
+            continue;
+        }
+        // (a residue view walks its dense causal layout once per residue class)
         for (int64_t r = 0; r < L->view_l; ++r)
-            for (int64_t blk = 0; blk + 1 < (int64_t)ptr.size(); ++blk, ++x) {
-                items[x] = Item{bh, (int32_t)blk, (int32_t)r, 0};
-                cost[x] = ptr[blk + 1] - ptr[blk];
+            for (int64_t blk = 0; blk + 1 < (int64_t)ptr.size(); ++blk) {
+                items.push_back(Item{bh, (int32_t)blk, (int32_t)r, -1});
+                cost.push_back(ptr[blk + 1] - ptr[blk]);
             }
     }
-    std::vector<size_t> order((size_t)count);
+    std::vector<size_t> order(items.size());
     std::iota(order.begin(), order.end(), 0);
     std::stable_sort(order.begin(), order.end(), [&](size_t u, size_t v) { return cost[u] > cost[v]; });
-    std::vector<Item> sorted((size_t)count);
-    for (size_t a = 0; a < (size_t)count; ++a) sorted[a] = items[order[a]];
+    std::vector<Item> sorted(items.size());
+    for (size_t x = 0; x < items.size(); ++x) sorted[x] = items[order[x]];
     *out = std::move(sorted);
 }
 

@@ -59,6 +59,8 @@ struct DevLayout {
     // 1 + h when the member's whole query list has allowed elements only in
     // its 32-key half h.
     const int32_t* kgrp_mode;
+    // Per key block: {its key-block pair, member (0 or 1)}.
+    const int2* kblk_grp;
     // Sequence view.  Row m of the sequence a work item walks is position
     // r + vl * m of its (batch, head), r the item's residue; rows m >= vm
     // (a ragged last block) are read clamped and never written.  A plain

@@ -168,10 +168,13 @@ int sa_layout_set_residue_view(sa_layout_t* lay, int enable);
  * the view on, sa_fwd and the sa_bwd calls run this layout's heads against
  * 64-key blocks of the summary keys (read in place, no copy): at n = 12288,
  * l = 128, c = 32 that is 4656 blocks per head, almost all full, against the
- * raster layout's 9216 half-empty ones.  The forward and the dQ stage walk
- * the view; the dK/dV stage keeps walking the raster layout, whose key blocks
- * have more and shorter query lists (in the view the first key blocks are
- * listed by nearly every query block).  The results are those of the raster
+ * raster layout's 9216 half-empty ones.  Every stage walks the view.  In the
+ * view the first key blocks are listed by nearly every query block, so the
+ * dK/dV stage walks each pair of key blocks in chunks of at most 96 query
+ * blocks, each chunk leaving fp32 partial sums in device memory the library
+ * keeps with the call's work list, and a second kernel adds each pair's
+ * chunks in a fixed order (deterministic) and writes dK, dV, with zeros on
+ * the positions no query reaches.  The results are those of the raster
  * layout (same pairs; only the rounding order differs).  The layout itself (sa_layout_info,
  * sa_layout_export) is unchanged.  enable = 0 turns the view off.
  *
@@ -240,7 +243,8 @@ size_t sa_bwd_workspace_size(int32_t B, int32_t H, int64_t n, int32_t d);
  * caller, contents ignored on entry.  Same errors as sa_fwd, plus
  * SA_ERR_INVALID_ARG when ws_bytes is too small.  Deterministic: no atomics,
  * so equal inputs give bitwise equal outputs.  Runs sa_bwd_dq_rowterms then
- * sa_bwd_dkdv (two kernels).
+ * sa_bwd_dkdv (two kernels; three with compact views, whose dK/dV chunks are
+ * summed by a third).
  */
 int sa_bwd(const sa_layout_t* const* head_layout, int32_t B, int32_t H, int64_t n, int32_t d,
            int dtype, float scale, const void* q, const void* k, const void* v, const void* o,
@@ -262,7 +266,8 @@ int sa_bwd(const sa_layout_t* const* head_layout, int32_t B, int32_t H, int64_t 
  * different streams, or from several threads without ordering) race and
  * give wrong gradients; calls ordered on one stream are safe.  The scratch
  * needs no clearing (the first kernel writes every row term the second
- * reads).
+ * reads).  Compact views' dK/dV partial sums use the buffer cached with the
+ * work list (made by that earlier sa_bwd), under the same rule.
  */
 int sa_bwd_noalloc(const sa_layout_t* const* head_layout, int32_t B, int32_t H, int64_t n, int32_t d,
                    int dtype, float scale, const void* q, const void* k, const void* v, const void* o,

@@ -9,6 +9,7 @@
 // Exit status 0 when every check passes (a sanitizer report aborts).
 #include <cstdio>
 #include <cstdlib>
+#include <algorithm>
 #include <vector>
 
 #include "pack.h"
@@ -71,7 +72,7 @@ void check_image(sa_layout* L, const char* what)
         for (int32_t B : {1, 3}) {
             sa_layout* hl[2] = {L, L};
             std::vector<Item> items;
-            build_work_items(kind, B, 2, hl, &items);
+            build_work_items(kind, B, 2, hl, 0, &items);
             const size_t per = kind == kByQuery ? L->row_ptr.size() - 1
                                : kind == kByQueryPair ? L->qgroups.ptr.size() - 1
                                                       : L->kgroups.ptr.size() - 1;
@@ -80,6 +81,29 @@ void check_image(sa_layout* L, const char* what)
                 CHECK(it.bh >= 0 && it.bh < B * 2 && it.blk >= 0 && (size_t)it.blk < per && it.r >= 0 &&
                           it.r < L->view_l,
                       "%s: item", what);
+        }
+    // A compact view's dK/dV list in chunks: every chunk inside its pair's
+    // list, the chunks of a pair covering it exactly, slots distinct.
+    if (is_compact(L))
+        for (int32_t steps : {1, 7, 64}) {
+            sa_layout* hl[2] = {L, L};
+            std::vector<Item> items;
+            DkdvSplit split;
+            build_work_items(kByKeyPair, 2, 2, hl, steps, &items, &split);
+            const size_t ng = L->kgroups.ptr.size() - 1;
+            CHECK(split.heads.size() == 4 && split.groups.size() == 4 * ng, "%s: split tables", what);
+            std::vector<int> seen((size_t)split.slots, 0);
+            for (const Item& it : items) {
+                CHECK(it.slot >= 0 && it.slot < split.slots && it.blk >= 0 && (size_t)it.blk < ng, "%s: chunk", what);
+                if (it.slot < 0 || it.slot >= split.slots || it.blk < 0 || (size_t)it.blk >= ng) continue;
+                ++seen[(size_t)it.slot];
+                const int32_t len = L->kgroups.ptr[it.blk + 1] - L->kgroups.ptr[it.blk];
+                const int2 gs = split.groups[(size_t)split.heads[(size_t)it.bh].y + (size_t)it.blk];
+                CHECK(split.heads[(size_t)it.bh].x == it.bh, "%s: head table", what);
+                CHECK(it.r == (it.slot - gs.x) * steps && (it.r < len || (len == 0 && it.r == 0)), "%s: chunk start", what);
+                CHECK(gs.y == std::max<int32_t>(1, (len + steps - 1) / steps), "%s: chunk count", what);
+            }
+            for (int x : seen) CHECK(x == 1, "%s: slot used %d times", what, x);
         }
 }
 

@@ -487,6 +487,9 @@ COMPACT = [
     ([("fixed_b", 256, 128)], 1024, 64, "c = 128: two key blocks per l-block"),
     ([("fixed_b", 128, 128)], 512, 64, "c = l: no gaps (dense causal)"),
     ([("fixed_b", 128, 32)], 1024, 128, "d = 128"),
+    ([("fixed_b", 32, 8)], 8192, 64, "query lists of 128 steps: the dK/dV kernel walks them in chunks"),
+    ([("fixed_b", 128, 64)], 12288, 64, "lists of 192 steps: two full chunks"),
+    ([("fixed_b", 64, 16)], 8192, 128, "d = 128, lists of 128 steps: a chunk of 96 and a ragged one"),
     ([("fixed_a", 128, 32), ("fixed_b", 128, 32), ("strided_b", 16, 1)], 1024, 64,
      "raster, compact and residue-view heads in one call"),
 ]
@@ -542,6 +545,18 @@ def test_compact_view_every_output_written():
     gap = (torch.arange(n, device=DEV) % 128) < 96  # non-summary positions of head 0
     assert torch.count_nonzero(dk[:, 0][:, gap]) == 0 and torch.count_nonzero(dv[:, 0][:, gap]) == 0
     assert torch.all(lse[:, 0, :96] == -math.inf) and torch.count_nonzero(o[:, 0, :96]) == 0
+
+
+def test_compact_view_bitwise_repeat():
+    """The compact view's dK/dV chunks are summed in a fixed order: two
+    runs agree bit for bit."""
+    pats, n, d = [("fixed_a", 32, 8), ("fixed_b", 32, 8)], 8192, 64
+    x = workloads.custom_inputs((2, 2, n, d), torch.bfloat16, seed=97)
+    lays = view_layouts(pats, n)
+    r1 = run(x, pats, 64, 1.0, backward=True, lays=lays)
+    r2 = run(x, pats, 64, 1.0, backward=True, lays=lays)
+    for t in ("o", "lse", "dq", "dk", "dv"):
+        assert torch.equal(r1[t], r2[t]), t
 
 
 def test_compact_view_full_size_sampled():
