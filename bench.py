@@ -43,6 +43,10 @@ def parse():
     ap.add_argument("--compact-view", action="store_true",
                     help="run fixed-B heads in their compact view (blocks of the summary keys only); the "
                          "metric then counts the compact view's blocks")
+    ap.add_argument("--views-path", action="store_true",
+                    help="after the timed steps, also time the same step with strided-B heads in the residue view "
+                         "and fixed-B heads in the compact view (reported as views_path; off by default so that a "
+                         "kernel trace of the default command holds only the timed launches)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-heads", type=int, default=0,
                     help="heads in the oracle sample (default: sized to ~10-30 s)")
@@ -140,14 +144,6 @@ def listed_blocks(lay):
     return v["nnz"] * (lay.l if v["kind"] == "residue" else 1)
 
 
-def listed_blocks_dkdv(lay):
-    """Blocks the dK/dV kernel walks for one head: as listed_blocks, but a
-    compact view's heads in their raster layout (that kernel does not walk
-    compact views)."""
-    v = lay.view_info()
-    return lay.info()["nnz"] if v["kind"] == "compact" else listed_blocks(lay)
-
-
 def compact_live_quadrants(lay):
     """Live 32 x 32 quadrants of a fixed-B compact view: query row i sees the
     first cnt(i) summary keys, so quadrant (query half rh, key half ch) of
@@ -169,7 +165,7 @@ def counted_flops(layouts, batch, T, d):
     return blocks * 4.0 * T * T * d, blocks
 
 
-def live_quadrants(layouts, batch, T, raster_compact=False):
+def live_quadrants(layouts, batch, T):
     """32 x 32 quadrants of the listed blocks that hold an allowed element,
     summed over (batch, head).  The block-64 kernels skip the others, so
     their matrix cores execute this many quadrants' products; the counted
@@ -181,7 +177,7 @@ def live_quadrants(layouts, batch, T, raster_compact=False):
             nb, nr = residue_blocks(lay)  # dense causal: 3 live quadrants on the diagonal
             total += nr * (3 * nb + 4 * (nb * (nb - 1) // 2))
             continue
-        if getattr(lay, "compact_view", False) and not raster_compact:
+        if getattr(lay, "compact_view", False):
             total += compact_live_quadrants(lay)
             continue
         ex = lay.export()
@@ -303,6 +299,56 @@ def cpu_baseline(w, x, pats, lays, T, max_heads, outputs=None, runs=3):
         "allowed_element_gflops": elements * w.d * (14.0 if w.backward else 4.0) / secs / 1e9,
         "parity": parity,
     }
+
+
+def views_step(w, pats, x, steps, warmup):
+    """The same step with every strided-B head in its residue view and every
+    fixed-B head (c a power of two) in its compact view -- the same allowed
+    pairs, walked as dense blocks -- on its own output buffers: step time
+    and the pattern's useful-pair rate.  None when no head has a view."""
+    import torch
+    import block_sparse_factorized_amd as sa
+    if not w.backward or w.block != 64:  # the views are walked by the block-64 kernels only
+        return None
+    dev = torch.device("cuda:0")
+    lays, cache, any_view = [], {}, False
+    for (p, l, c) in pats:
+        if (p, l, c) not in cache:
+            lay = sa.sa_layout_build(p, w.n, l, c, block=w.block)
+            if p == "strided_b" and w.n % l == 0:
+                lay.set_residue_view(True)
+                any_view = True
+            elif p == "fixed_b" and w.n % l == 0 and (c & (c - 1)) == 0:
+                lay.set_compact_view(True)
+                any_view = True
+            cache[(p, l, c)] = lay
+        lays.append(cache[(p, l, c)])
+    if not any_view:
+        return None
+    q, k, v, do = (x[t].to(dev) for t in ("q", "k", "v", "do"))
+    o = torch.empty_like(q)
+    lse = torch.empty(q.shape[:3], dtype=torch.float32, device=dev)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(q), torch.empty_like(q)
+    ws = torch.empty(max(sa.sa_bwd_workspace_size(w.batch, w.heads, w.n, w.d), 16), dtype=torch.uint8, device=dev)
+
+    def step():
+        sa.sa_fwd(q, k, v, lays, 1.0, o=o, lse=lse)
+        sa.sa_bwd(q, k, v, o, lse, do, lays, 1.0, dq=dq, dk=dk, dv=dv, workspace=ws)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        step()
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / steps
+    allowed = sum(lay.info()["allowed"] for lay in lays) * w.batch
+    return {"ms_per_step": ms, "useful_pair_tflops": allowed * w.d * 14.0 / (ms * 1e-3) / 1e12,
+            "views": sorted(set(lay.view_info()["kind"] for lay in lays) - {"layout"}),
+            "what": "the same step with strided-B heads in the residue view and fixed-B heads in the compact "
+                    "view (same allowed pairs, fewer and denser blocks); not the metric, which counts the "
+                    "layouts' blocks"}
 
 
 def length_scaling(args):
@@ -511,15 +557,12 @@ def main():
     # Matrix-core flops the kernels execute, per live 32 x 32 quadrant
     # (forward S, PV; dK/dV S, dP, dV, dK; dQ S, dP, dQ).
     # The fp32 block-16 kernel skips nothing: it executes what is counted.
-    # (The dK/dV kernel walks compact-view heads in their raster layout.)
     quads = live_quadrants(lays, w.batch, T)
-    quads_kv = live_quadrants(lays, w.batch, T, raster_compact=True) if args.compact_view else quads
-    blocks_kv = sum(listed_blocks_dkdv(lay) for lay in lays) * w.batch
     per_quad = {"fwd": 4.0, "bwd_dkdv": 8.0, "bwd_dq": 6.0}
     kernels = {}
     for nm in names:
         avg_s = float(kernel_ms[nm].mean()) * 1e-3
-        nb, nq = (blocks_kv, quads_kv) if nm == "bwd_dkdv" else (blocks, quads)
+        nb, nq = blocks, quads
         fl = per_block[nm] * T * T * d * nb
         ex = per_quad[nm] * 32 * 32 * d * nq if T == 64 else fl
         kernels[nm] = {"avg_us": avg_s * 1e6, "median_us": float(np.median(kernel_ms[nm])) * 1e3,
@@ -540,6 +583,9 @@ def main():
     }
     dk_ = kernels[dominant]
     kern_file = "fwd.hip" if dominant == "fwd" else "bwd.hip"
+    # The fastest walk of the same pairs, when the layouts have views (after
+    # the timed steps, on its own buffers).
+    fastest = views_step(w, pats, x, max(5, args.steps // 2), 3) if args.views_path and not views else None
     # The machine's own denominators, measured after the timed steps.
     mp = measured_peaks() if w.dtype == "bf16" else None
     mpeak = mp["mfma_bf16_tflops"] if mp else None
@@ -608,6 +654,7 @@ def main():
         "fwd_frac_of_measured_peak": kernels["fwd"]["tflops"] / mpeak if mpeak else None,
         "layout_build_ms": layout_ms,
         "roofline": roofline,
+        "views_path": dict(fastest, speedup_vs_layouts=ms_per_step / fastest["ms_per_step"]) if fastest else None,
         "cpu_baseline": None,
         "parity": None,
     }
