@@ -108,8 +108,8 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(const BwdArgs a)
     const int n32 = lane & 31, hh = lane >> 5;
     const Item item = ld_uniform(&a.items[blockIdx.x]);
     const int bh = item.bh, grp = item.blk;
-    // A chunk of a compact view's query list: steps item.r .. +chunk_steps-1,
-    // summed into partial-sum slot item.slot (no residue class).
+    // A chunk of a long query list (slot >= 0: chunk_tab[slot] = {first
+    // step, steps}) leaves fp32 partial sums in its slot for a summing pass.
     const bool chunk = item.slot >= 0;
     const int res = chunk ? 0 : item.r;
     const DevLayout L = a.heads.lay[a.heads.head_lay[bh % a.H]];
@@ -175,8 +175,12 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(const BwdArgs a)
     }
     const int g0 = ld_uniform(&L.kgrp_ptr[grp]);
     const int glen = ld_uniform(&L.kgrp_ptr[grp + 1]) - g0;
-    const int p0 = chunk ? g0 + item.r : g0;
-    const int nblk = chunk ? min(a.chunk_steps, glen - item.r) : glen;
+    int p0 = g0, nblk = glen;
+    if (chunk) {
+        const int2 ct = ld_uniform(&a.chunk_tab[item.slot]);
+        p0 += ct.x;
+        nblk = ct.y;
+    }
     const float c2 = a.scale_log2;
 
     // Starts the loads of query tile qb into (qd, od) and returns this lane's
@@ -489,6 +493,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D == 64 ? 4
     const int n32 = lane & 31, hh = lane >> 5;
     const Item item = ld_uniform(&a.items[blockIdx.x]);
     const int bh = item.bh, grp = item.blk;
+    // A chunk of a long key list (slot >= 0: chunk_tab[slot] = {first step,
+    // steps}) leaves its fp32 dQ in its slot for the combining pass.
+    const bool chunk = item.slot >= 0;
+    const int2 ct = chunk ? ld_uniform(&a.chunk_tab[item.slot]) : make_int2(0, 0);
     const DevLayout L = a.heads.lay[a.heads.head_lay[bh % a.H]];
     const int2 pair = ld_uniform(&L.qgrp_blk[grp]);
     const int qb = member ? pair.y : pair.x;  // -1: this wave has no rows
@@ -498,8 +506,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D == 64 ? 4
     // are read clamped (and masked out).
     const int vl = L.vl, vm = L.vm, km = L.km;
     const int rs = vl * D;
-    const int64_t head = (int64_t)bh * a.n * D + (int64_t)item.r * D;
-    const int64_t lrow0 = (int64_t)bh * a.n + item.r;  // row-term index of row 0
+    const int res = chunk ? 0 : item.r;
+    const int64_t head = (int64_t)bh * a.n * D + (int64_t)res * D;
+    const int64_t lrow0 = (int64_t)bh * a.n + res;  // row-term index of row 0
     const unsigned short* K = (const unsigned short*)a.k + head;
     const unsigned short* V = (const unsigned short*)a.v + head;
     const int q_local = 32 * wr + n32;
@@ -537,7 +546,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D == 64 ? 4
         nd_i = -(acc + swap_halves(acc));
         const float l = a.lse[lrow0 + trow];
         nl2 = l == -INFINITY ? -INFINITY : -l * kLog2e;
-        if (hh == 0 && qb >= 0 && q_row < vm) {
+        // (every chunk of a list forms the same row terms; its first writes them)
+        if (hh == 0 && qb >= 0 && q_row < vm && ct.x == 0) {
             a.ndelta[lrow0 + trow] = nd_i;
             a.nl2[lrow0 + trow] = nl2;
         }
@@ -563,8 +573,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D == 64 ? 4
     f32x16 dq[D / 32];
 #pragma unroll
     for (int dt = 0; dt < D / 32; ++dt) zero(dq[dt]);
-    const int p0 = ld_uniform(&L.qgrp_ptr[grp]);
-    const int nblk = ld_uniform(&L.qgrp_ptr[grp + 1]) - p0;
+    int p0 = ld_uniform(&L.qgrp_ptr[grp]);
+    int nblk = ld_uniform(&L.qgrp_ptr[grp + 1]) - p0;
+    if (chunk) {
+        p0 += ct.x;
+        nblk = ct.y;
+    }
     const float c2 = a.scale_log2;
 
     auto issue = [&](int kb, unsigned char* kd, unsigned char* vd) {
@@ -715,7 +729,17 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D == 64 ? 4
         if (t + 1 < nblk) step_tile(t + 1, kbuf1, vbuf1, kbuf0, vbuf0);
     }
 
-    if (qb < 0 || q_row >= vm) return;  // no rows, or a ragged block's padding row
+    if (qb < 0) return;  // no rows
+    if (chunk) {
+        // this chunk's (unscaled) dQ registers, 64 lanes wide, for the combining pass
+        float* P = a.partials + (int64_t)item.slot * kDqSlotFloats(D) + (int64_t)w * (D / 32) * 16 * 64 + lane;
+#pragma unroll
+        for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) P[(dt * 16 + i) * 64] = dq[dt][i];
+        return;
+    }
+    if (q_row >= vm) return;  // a ragged block's padding row
     unsigned short* DQ = (unsigned short*)a.dq + head + (uint32_t)(q_row * rs);
 #pragma unroll
     for (int dt = 0; dt < D / 32; ++dt)
@@ -726,6 +750,93 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D == 64 ? 4
             u[1] = bf16_pair(dq[dt][4 * g + 2] * a.scale, dq[dt][4 * g + 3] * a.scale);
             *(u32x2*)(DQ + 32 * dt + 8 * g + 4 * hh) = u;
         }
+}
+
+// ---------------------------------------------------------------------------
+// Combining pass of the dQ kernel's chunks: each chunked query-block pair's
+// rows get the sum of its chunks' fp32 dQ, taken in list order, scaled and
+// rounded to bf16 (what one pass over the whole list writes, up to the
+// order of the sum).  Wave and lane as in the dQ kernel.
+template <int D>
+__global__ __launch_bounds__(256) void dq_combine_kernel(const CombineArgs a)
+{
+    constexpr int T = 64, NR = (D / 32) * 16;
+    const int lane = threadIdx.x & 63;
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int member = w >> 1, wr = w & 1;
+    const int n32 = lane & 31, hh = lane >> 5;
+    const int4 g = ld_uniform(&a.groups[blockIdx.x]);  // {bh, pair, first slot, chunks}
+    const DevLayout L = a.heads.lay[a.heads.head_lay[g.x % a.H]];
+    const int2 pair = ld_uniform(&L.qgrp_blk[g.y]);
+    const int qb = member ? pair.y : pair.x;
+    if (qb < 0) return;
+    const int q_row = qb * T + 32 * wr + n32;
+    if (q_row >= L.vm) return;
+    const float* P0 = a.partials + (int64_t)g.z * kDqSlotFloats(D) + (int64_t)w * NR * 64 + lane;
+    f32x16 acc[D / 32];
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt) zero(acc[dt]);
+    for (int c = 0; c < g.w; ++c) {
+        const float* P = P0 + (int64_t)c * kDqSlotFloats(D);
+#pragma unroll
+        for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) acc[dt][i] += P[(dt * 16 + i) * 64];
+    }
+    unsigned short* DQ = (unsigned short*)a.out0 + (int64_t)g.x * a.n * D + (uint32_t)(q_row * L.vl * D);
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+        for (int gg = 0; gg < 4; ++gg) {
+            u32x2 u;
+            u[0] = bf16_pair(acc[dt][4 * gg] * a.scale, acc[dt][4 * gg + 1] * a.scale);
+            u[1] = bf16_pair(acc[dt][4 * gg + 2] * a.scale, acc[dt][4 * gg + 3] * a.scale);
+            *(u32x2*)(DQ + 32 * dt + 8 * gg + 4 * hh) = u;
+        }
+}
+
+// Combining pass of the dK/dV kernel's chunks of plain layouts: each chunked
+// key-block pair's rows (both members, the valid rows of a ragged last
+// block) get the sums of its chunks' fp32 partials ([dK, dV][member][key][d]
+// per slot), taken in list order; dK scaled; both rounded to bf16.  D/8
+// threads per row, 8 consecutive elements each.
+template <int D>
+__global__ __launch_bounds__(256) void dkdv_combine_kernel(const CombineArgs a)
+{
+    constexpr int TPR = D / 8, RPP = 256 / TPR;  // threads per row, rows per pass
+    const int4 g = ld_uniform(&a.groups[blockIdx.x]);  // {bh, pair, first slot, chunks}
+    const DevLayout L = a.heads.lay[a.heads.head_lay[g.x % a.H]];
+    const int2 pair = ld_uniform(&L.kgrp_blk[g.y]);
+    const int part = threadIdx.x % TPR;
+    for (int pass = 0; pass < 128 / RPP; ++pass) {
+        const int rr = pass * RPP + threadIdx.x / TPR;  // member * 64 + key
+        const int member = rr >> 6, key = rr & 63;
+        const int kb = member ? pair.y : pair.x;
+        if (kb < 0) continue;
+        const int row = kb * 64 + key;
+        if (row >= L.vm) continue;
+        f32x4 k0 = {0.f, 0.f, 0.f, 0.f}, k1 = k0, v0 = k0, v1 = k0;
+        const int64_t e = (int64_t)rr * D + 8 * part;
+        for (int c = 0; c < g.w; ++c) {
+            const float* P = a.partials + (int64_t)(g.z + c) * kSlotFloats(D) + e;
+            k0 += *(const f32x4*)P;
+            k1 += *(const f32x4*)(P + 4);
+            v0 += *(const f32x4*)(P + 2 * 64 * D);
+            v1 += *(const f32x4*)(P + 2 * 64 * D + 4);
+        }
+        const int64_t o = (int64_t)g.x * a.n * D + (int64_t)row * L.vl * D + 8 * part;
+        u32x4 uk, uv;
+        uk[0] = bf16_pair(k0[0] * a.scale, k0[1] * a.scale);
+        uk[1] = bf16_pair(k0[2] * a.scale, k0[3] * a.scale);
+        uk[2] = bf16_pair(k1[0] * a.scale, k1[1] * a.scale);
+        uk[3] = bf16_pair(k1[2] * a.scale, k1[3] * a.scale);
+        uv[0] = bf16_pair(v0[0], v0[1]);
+        uv[1] = bf16_pair(v0[2], v0[3]);
+        uv[2] = bf16_pair(v1[0], v1[1]);
+        uv[3] = bf16_pair(v1[2], v1[3]);
+        *(u32x4*)((unsigned short*)a.out0 + o) = uk;
+        *(u32x4*)((unsigned short*)a.out1 + o) = uv;
+    }
 }
 
 }  // namespace
@@ -777,5 +888,25 @@ hipError_t launch_bwd_dq_bf16_t64(int d, const BwdArgs& a, int n_items, bool row
         hipLaunchKernelGGL((bwd_dq_kernel<128, false, false>), g, b, 0, stream, a);
     return hipGetLastError();
 }
+
+hipError_t launch_dq_combine_bf16(int d, const CombineArgs& a, int n_groups, hipStream_t stream)
+{
+    if (d == 64)
+        hipLaunchKernelGGL(dq_combine_kernel<64>, dim3(n_groups), dim3(256), 0, stream, a);
+    else
+        hipLaunchKernelGGL(dq_combine_kernel<128>, dim3(n_groups), dim3(256), 0, stream, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_dkdv_combine_bf16(int d, const CombineArgs& a, int n_groups, hipStream_t stream)
+{
+    if (d == 64)
+        hipLaunchKernelGGL(dkdv_combine_kernel<64>, dim3(n_groups), dim3(256), 0, stream, a);
+    else
+        hipLaunchKernelGGL(dkdv_combine_kernel<128>, dim3(n_groups), dim3(256), 0, stream, a);
+    return hipGetLastError();
+}
+
+
 
 }  // namespace sa

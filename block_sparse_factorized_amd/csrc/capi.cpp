@@ -65,7 +65,7 @@ int device_layout(sa_layout* L, int dev, DevLayout* out, bool upload)
 
 // ---------------------------------------------------------------------------
 // Work lists (build_work_items), uploaded once and cached per (kind, device,
-// B, H, layouts).
+// B, H, d, layouts, chunking).
 
 // Steps per chunk of a compact view's query list in the dK/dV kernel: long
 // enough to amortise a chunk's partial sums, short enough that the first
@@ -79,84 +79,184 @@ struct Plan {
     Item* items;
     int count;
     int dev;
-    void* mem;  // the one allocation behind everything below
-    // dK/dV of compact views (kByKeyPair only): the summing pass's tables
-    // (see ReduceArgs) and the chunks' partial sums.
-    const int2* rheads;
-    int n_rheads;
-    const int2* rgroups;
-    float* partials;
+    void* mem;  // the one allocation behind items and the tables below
+    // Chunks (see Split): the slot table, the chunked lists of plain layouts
+    // (combining pass) and the compact views' summing-pass tables (dK/dV).
+    const int2* chunk_tab;
+    const int4* groups;
+    int n_groups;
+    const int2* cheads;
+    int n_cheads;
+    const int2* cgroups;
+    size_t part_bytes;  // the chunks' partial results: slots x slot size
+    float* partials;    // the buffer of the call's stream (get_plan)
+};
+
+// A cached work list and the partial-result buffers of the streams that
+// have run it: calls on one stream are ordered, so they may share a buffer;
+// calls on different streams may overlap, so each stream gets its own.
+struct PlanEntry {
+    Plan plan;
+    std::map<void*, void*> parts;  // stream -> partial buffer
 };
 
 std::mutex g_plan_mu;
-std::map<std::string, Plan, std::less<>> g_plans;  // looked up by string_view: no allocation
+std::map<std::string, PlanEntry, std::less<>> g_plans;  // looked up by string_view: no allocation
 // layout serial -> keys of the cached work lists that name it; destroying the
 // layout frees them (sa_layout_destroy), so a process that keeps building and
 // destroying layouts does not accumulate work lists.
 std::map<uint64_t, std::vector<std::string>> g_plan_keys;
 
+// sa_set_split: 0 chunk lengths by the rule below, -1 no chunks of plain
+// layouts' lists, k > 0 every plain list longer than k in chunks of <= k.
+std::atomic<int> g_split{0};
+
 // The cache key of a work list, written into buf (no allocation); returns its length.
-size_t plan_key(char* buf, size_t cap, ListKind kind, int dev, int32_t B, int32_t H, int32_t d, sa_layout* const* hl)
+size_t plan_key(char* buf, size_t cap, ListKind kind, int dev, int32_t B, int32_t H, int32_t d, int split,
+                sa_layout* const* hl)
 {
-    size_t len = (size_t)snprintf(buf, cap, "%d:%d:%d:%d:%d", (int)kind, dev, B, H, d);
+    size_t len = (size_t)snprintf(buf, cap, "%d:%d:%d:%d:%d:%d", (int)kind, dev, B, H, d, split);
     for (int32_t h = 0; h < H && len < cap; ++h)
         len += (size_t)snprintf(buf + len, cap - len, ":%llu", (unsigned long long)hl[h]->serial);
     return std::min(len, cap - 1);
 }
 
-// The work list of a call, built and uploaded on first use.  create = false:
-// only look it up (no allocation); SA_ERR_UNSUPPORTED when it is not cached.
-int get_plan(ListKind kind, int dev, int32_t B, int32_t H, int32_t d, sa_layout* const* hl, Plan* out, bool create)
+// Chunk length for the lists of plain layouts, and the length a list must
+// exceed to be cut (*min_len).  The workgroups of a compute unit share its
+// SIMDs, so a unit's time follows the steps it is given, not the number of
+// its workgroups: as long as every unit holds several times the longest
+// list, the longest-first order leaves their loads even and chunks only add
+// work (their partial results and the combining pass).  Chunks pay where one
+// list is longer than the other units' whole loads -- few heads and a batch
+// of one, where some units would idle: a list longer than twice the average
+// load of a unit is cut into chunks of that length (at least 16 steps).
+// Measured (one box, fwd + dQ + dK/dV): B = 1, two strided heads, n = 8192:
+// 149 -> 86 us; B = 1, two fixed heads, n = 16384: 381 -> 138 us; the five
+// workloads (every unit holding 12 to 100 times the longest list) unchanged
+// by this rule, and 2-35 % slower with chunks forced on.
+int32_t plain_chunk(ListKind kind, int dev, int32_t B, int32_t H, sa_layout* const* hl, int split, int32_t* min_len)
 {
-    char kbuf[48 + 21 * kMaxHeads];  // "kind:dev:B:H:d" + ":serial" per head
-    const size_t klen = plan_key(kbuf, sizeof kbuf, kind, dev, B, H, d, hl);
+    *min_len = 0;
+    if (kind == kByQuery || split < 0) return 0;
+    if (split > 0) {
+        *min_len = split;
+        return split;
+    }
+    int cus = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) return 0;
+    int64_t total = 0;
+    for (int32_t h = 0; h < H; ++h) {
+        const std::vector<int32_t>& ptr = kind == kByKeyPair ? hl[h]->kgroups.ptr : hl[h]->qgroups.ptr;
+        if (!ptr.empty()) total += (int64_t)(ptr.back() - ptr.front()) * hl[h]->view_l;
+    }
+    total *= B;
+    const double cs = std::max(16.0, std::ceil(2.0 * (double)total / (double)cus));
+    if (cs > (double)(1 << 30)) return 0;
+    *min_len = (int32_t)cs;
+    return (int32_t)cs;
+}
+
+// The work list of a call, built and uploaded on first use, with the
+// partial-result buffer of `stream`.  create = false: only look them up (no
+// allocation); SA_ERR_UNSUPPORTED when the list is not cached.  A stream
+// with no buffer of its own gets one, unless nothing may be allocated
+// (create = false) or the stream is being captured into a graph: then a
+// buffer made for another stream serves (calls that share it must not
+// overlap), and SA_ERR_UNSUPPORTED when there is none.
+int get_plan(ListKind kind, int dev, int32_t B, int32_t H, int32_t d, sa_layout* const* hl, void* stream, Plan* out,
+             bool create)
+{
+    const int split = g_split.load(std::memory_order_relaxed);
+    char kbuf[64 + 21 * kMaxHeads];  // "kind:dev:B:H:d:split" + ":serial" per head
+    const size_t klen = plan_key(kbuf, sizeof kbuf, kind, dev, B, H, d, split, hl);
     std::lock_guard<std::mutex> g(g_plan_mu);
     auto it = g_plans.find(std::string_view(kbuf, klen));
-    if (it != g_plans.end()) {
-        *out = it->second;
-        return SA_OK;
+    if (it == g_plans.end()) {
+        if (!create)
+            return fail(SA_ERR_UNSUPPORTED, "no cached work list for this (B, H, layouts) on device %d (one call of "
+                        "sa_bwd with the same arguments caches it)", dev);
+        const std::string key(kbuf, klen);
+        int32_t min_len = 0;
+        const int32_t cs = plain_chunk(kind, dev, B, H, hl, split, &min_len);
+        std::vector<Item> sorted;
+        Split sp;
+        build_work_items(kind, B, H, hl, kind == kByKeyPair ? kChunkSteps : 0, cs, min_len, &sorted, &sp);
+        const int64_t count = (int64_t)sorted.size();
+        // One allocation: items, then the chunk tables, each 256-byte aligned.
+        auto al = [](size_t x) { return (x + 255) & ~(size_t)255; };
+        const size_t off_tab = al(sorted.size() * sizeof(Item));
+        const size_t off_groups = al(off_tab + sp.chunk_tab.size() * sizeof(int2));
+        const size_t off_cheads = al(off_groups + sp.groups.size() * sizeof(int4));
+        const size_t off_cgroups = al(off_cheads + sp.cheads.size() * sizeof(int2));
+        const size_t total = al(off_cgroups + sp.cgroups.size() * sizeof(int2));
+        std::vector<unsigned char> host(total, 0);
+        auto put = [&](size_t off, const void* src, size_t bytes) {
+            if (bytes) memcpy(host.data() + off, src, bytes);
+        };
+        put(0, sorted.data(), sorted.size() * sizeof(Item));
+        put(off_tab, sp.chunk_tab.data(), sp.chunk_tab.size() * sizeof(int2));
+        put(off_groups, sp.groups.data(), sp.groups.size() * sizeof(int4));
+        put(off_cheads, sp.cheads.data(), sp.cheads.size() * sizeof(int2));
+        put(off_cgroups, sp.cgroups.data(), sp.cgroups.size() * sizeof(int2));
+        void* mem = nullptr;
+        hipError_t e = hipMalloc(&mem, std::max<size_t>(total, 256));
+        if (e != hipSuccess) return fail(SA_ERR_ALLOC, "work list: hipMalloc(%zu): %s", total, hipGetErrorString(e));
+        e = hipMemcpy(mem, host.data(), total, hipMemcpyHostToDevice);
+        if (e != hipSuccess) {
+            (void)hipFree(mem);
+            return hip_fail(e, "work list: hipMemcpy");
+        }
+        const int64_t slot_floats = kind == kByKeyPair ? kSlotFloats(d) : kind == kByQueryPairDq ? kDqSlotFloats(d)
+                                                                                                  : kFwdSlotFloats(d);
+        unsigned char* base = (unsigned char*)mem;
+        Plan p{};
+        p.items = (Item*)mem;
+        p.count = (int)count;
+        p.dev = dev;
+        p.mem = mem;
+        p.chunk_tab = (const int2*)(base + off_tab);
+        p.groups = (const int4*)(base + off_groups);
+        p.n_groups = (int)sp.groups.size();
+        p.cheads = (const int2*)(base + off_cheads);
+        p.n_cheads = (int)sp.cheads.size();
+        p.cgroups = (const int2*)(base + off_cgroups);
+        p.part_bytes = (size_t)sp.slots * (size_t)slot_floats * sizeof(float);
+        p.partials = nullptr;
+        it = g_plans.emplace(key, PlanEntry{p, {}}).first;
+        for (int32_t h = 0; h < H; ++h) {
+            std::vector<std::string>& keys = g_plan_keys[hl[h]->serial];
+            if (keys.empty() || keys.back() != key) keys.push_back(key);
+        }
     }
-    if (!create)
-        return fail(SA_ERR_UNSUPPORTED, "no cached work list for this (B, H, layouts) on device %d (one call of "
-                    "sa_bwd with the same arguments caches it)", dev);
-    const std::string key(kbuf, klen);
-    std::vector<Item> sorted;
-    DkdvSplit split;
-    build_work_items(kind, B, H, hl, kind == kByKeyPair ? kChunkSteps : 0, &sorted, &split);
-    const int64_t count = (int64_t)sorted.size();
-    // One allocation: items, then (dK/dV of compact views) the summing
-    // pass's tables and the partial sums, each 256-byte aligned.
-    auto al = [](size_t x) { return (x + 255) & ~(size_t)255; };
-    const size_t off_heads = al(sorted.size() * sizeof(Item));
-    const size_t off_groups = al(off_heads + split.heads.size() * sizeof(int2));
-    const size_t off_part = al(off_groups + split.groups.size() * sizeof(int2));
-    const size_t total = off_part + (size_t)split.slots * (size_t)kSlotFloats(d) * sizeof(float);
-    std::vector<unsigned char> host(off_part, 0);
-    if (!sorted.empty()) memcpy(host.data(), sorted.data(), sorted.size() * sizeof(Item));
-    if (!split.heads.empty()) memcpy(host.data() + off_heads, split.heads.data(), split.heads.size() * sizeof(int2));
-    if (!split.groups.empty())
-        memcpy(host.data() + off_groups, split.groups.data(), split.groups.size() * sizeof(int2));
-    void* mem = nullptr;
-    hipError_t e = hipMalloc(&mem, std::max<size_t>(total, 256));
-    if (e != hipSuccess) return fail(SA_ERR_ALLOC, "work list: hipMalloc(%zu): %s", total, hipGetErrorString(e));
-    e = hipMemcpy(mem, host.data(), off_part, hipMemcpyHostToDevice);
-    if (e != hipSuccess) {
-        (void)hipFree(mem);
-        return hip_fail(e, "work list: hipMemcpy");
+    PlanEntry& pe = it->second;
+    *out = pe.plan;
+    if (pe.plan.part_bytes) {
+        auto b = pe.parts.find(stream);
+        if (b == pe.parts.end()) {
+            hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+            if (create && hipStreamIsCapturing((hipStream_t)stream, &cs) != hipSuccess)
+                cs = hipStreamCaptureStatusNone;
+            if (!create || cs != hipStreamCaptureStatusNone) {
+                if (pe.parts.empty())
+                    return fail(SA_ERR_UNSUPPORTED, "no partial-result buffer for this work list on device %d yet "
+                                "(one uncaptured call on the device makes it)", dev);
+                b = pe.parts.begin();
+            } else {
+                void* buf = nullptr;
+                hipError_t e = hipMalloc(&buf, pe.plan.part_bytes);
+                if (e != hipSuccess)
+                    return fail(SA_ERR_ALLOC, "partial results: hipMalloc(%zu): %s", pe.plan.part_bytes,
+                                hipGetErrorString(e));
+                b = pe.parts.emplace(stream, buf).first;
+            }
+        }
+        out->partials = (float*)b->second;
     }
-    unsigned char* base = (unsigned char*)mem;
-    Plan p{(Item*)mem, (int)count, dev, mem, (const int2*)(base + off_heads), (int)split.heads.size(),
-           (const int2*)(base + off_groups), split.slots ? (float*)(base + off_part) : nullptr};
-    g_plans[key] = p;
-    for (int32_t h = 0; h < H; ++h) {
-        std::vector<std::string>& keys = g_plan_keys[hl[h]->serial];
-        if (keys.empty() || keys.back() != key) keys.push_back(key);
-    }
-    *out = p;
     return SA_OK;
 }
 
-// Frees the cached work lists that name layout `serial`.
+// Frees the cached work lists that name layout `serial`, with their
+// partial-result buffers.
 void release_plans(uint64_t serial)
 {
     std::lock_guard<std::mutex> g(g_plan_mu);
@@ -166,8 +266,9 @@ void release_plans(uint64_t serial)
         auto p = g_plans.find(key);
         if (p == g_plans.end()) continue;
         int cur = 0;
-        if (hipGetDevice(&cur) == hipSuccess && hipSetDevice(p->second.dev) == hipSuccess) {
-            (void)hipFree(p->second.mem);
+        if (hipGetDevice(&cur) == hipSuccess && hipSetDevice(p->second.plan.dev) == hipSuccess) {
+            (void)hipFree(p->second.plan.mem);
+            for (auto& kv : p->second.parts) (void)hipFree(kv.second);
             (void)hipSetDevice(cur);
         }
         g_plans.erase(p);
@@ -389,7 +490,7 @@ int sa_fwd(const sa_layout_t* const* head_layout, int32_t B, int32_t H, int64_t 
     st = prepare_device(distinct, nl, &ht, &dev, true);
     if (st != SA_OK) return st;
     Plan plan;
-    st = get_plan(dtype == SA_BF16 ? kByQueryPair : kByQuery, dev, B, H, d, hl, &plan, true);
+    st = get_plan(dtype == SA_BF16 ? kByQueryPair : kByQuery, dev, B, H, d, hl, stream, &plan, true);
     if (st != SA_OK) return st;
     FwdArgs a;
     a.q = q;
@@ -403,6 +504,8 @@ int sa_fwd(const sa_layout_t* const* head_layout, int32_t B, int32_t H, int64_t 
     a.scale_log2 = scale * 1.4426950408889634f;
     a.items = plan.items;
     a.heads = ht;
+    a.chunk_tab = plan.chunk_tab;
+    a.partials = plan.partials;
     // The paired form when most of the walk's wave-steps have both halves
     // live (full blocks: dense layouts, residue views, wide strided A).  A
     // residue view's layout is walked once per residue class, view_l times
@@ -419,6 +522,21 @@ int sa_fwd(const sa_layout_t* const* head_layout, int32_t B, int32_t H, int64_t 
                        ? launch_fwd_bf16_t64(d, a, plan.count, paired, (hipStream_t)stream)
                        : launch_fwd_f32_t16(d, a, plan.count, (hipStream_t)stream);
     if (e != hipSuccess) return hip_fail(e, "sa_fwd: kernel launch");
+    if (plan.n_groups > 0) {
+        // the chunks of long lists: combined in list order
+        CombineArgs c{};
+        c.out0 = o;
+        c.lse = lse;
+        c.partials = plan.partials;
+        c.groups = plan.groups;
+        c.n = n;
+        c.H = H;
+        c.scale = scale;
+        c.scale_log2 = a.scale_log2;
+        c.heads = ht;
+        e = launch_fwd_combine_bf16(d, c, plan.n_groups, (hipStream_t)stream);
+        if (e != hipSuccess) return hip_fail(e, "sa_fwd: combining launch");
+    }
     return SA_OK;
 }
 
@@ -469,11 +587,11 @@ int bwd_call(const char* fn, int stages, const sa_layout_t* const* head_layout, 
     if (st != SA_OK) return st;
     Plan pk{}, pq{};
     if (kv) {
-        st = get_plan(kByKeyPair, dev, B, H, d, hl, &pk, alloc);
+        st = get_plan(kByKeyPair, dev, B, H, d, hl, stream, &pk, alloc);
         if (st != SA_OK) return st;
     }
     if (dqs) {
-        st = get_plan(kByQueryPair, dev, B, H, d, hl, &pq, alloc);
+        st = get_plan(kByQueryPairDq, dev, B, H, d, hl, stream, &pq, alloc);
         if (st != SA_OK) return st;
     }
     BwdArgs a;
@@ -495,19 +613,38 @@ int bwd_call(const char* fn, int stages, const sa_layout_t* const* head_layout, 
     a.scale_log2 = scale * 1.4426950408889634f;
     a.heads = ht;
     a.items = nullptr;
-    a.partials = pk.partials;
-    a.chunk_steps = kChunkSteps;
+    a.chunk_tab = nullptr;
+    a.partials = nullptr;
     hipStream_t s = (hipStream_t)stream;
     hipError_t e;
+    // The combining pass of a plan's chunked plain lists.
+    auto combine = [&](const Plan& p, bool dkdv) -> hipError_t {
+        CombineArgs c{};
+        c.out0 = dkdv ? dk : dq;
+        c.out1 = dv;
+        c.partials = p.partials;
+        c.groups = p.groups;
+        c.n = n;
+        c.H = H;
+        c.scale = scale;
+        c.scale_log2 = a.scale_log2;
+        c.heads = ht;
+        return dkdv ? launch_dkdv_combine_bf16(d, c, p.n_groups, s) : launch_dq_combine_bf16(d, c, p.n_groups, s);
+    };
     // The dQ kernel's one-element form pays off where such quadrants occur
     // (strided B); elsewhere the plain form keeps its grouped operand reads.
     bool one = false;
     for (int x = 0; x < nl; ++x) one = one || distinct[x]->one_quads;
     if (dq_rt) {
         a.items = pq.items;
-        a.heads = ht;
+        a.chunk_tab = pq.chunk_tab;
+        a.partials = pq.partials;
         e = launch_bwd_dq_bf16_t64(d, a, pq.count, true, one, s);
         if (e != hipSuccess) return hip_fail(e, "sa_bwd: dQ kernel launch");
+        if (pq.n_groups > 0) {
+            e = combine(pq, false);
+            if (e != hipSuccess) return hip_fail(e, "sa_bwd: dQ combining launch");
+        }
     }
     if (rt) {
         e = launch_bwd_rowterms_bf16(d, a, (int64_t)B * H * n, s);
@@ -515,30 +652,40 @@ int bwd_call(const char* fn, int stages, const sa_layout_t* const* head_layout, 
     }
     if (kv) {
         a.items = pk.items;
-        a.heads = ht;
+        a.chunk_tab = pk.chunk_tab;
+        a.partials = pk.partials;
         e = launch_bwd_dkdv_bf16_t64(d, a, pk.count, s);
         if (e != hipSuccess) return hip_fail(e, "sa_bwd: dK/dV kernel launch");
-        if (pk.n_rheads > 0) {
+        if (pk.n_cheads > 0) {
             // compact views: sum each key-block pair's chunks in order
             ReduceArgs r;
             r.dk = dk;
             r.dv = dv;
             r.partials = pk.partials;
-            r.heads_tab = pk.rheads;
-            r.groups = pk.rgroups;
+            r.heads_tab = pk.cheads;
+            r.groups = pk.cgroups;
             r.n = n;
             r.H = H;
             r.scale = scale;
             r.heads = ht;
-            e = launch_bwd_dkdv_reduce_bf16(d, r, pk.n_rheads, n, s);
+            e = launch_bwd_dkdv_reduce_bf16(d, r, pk.n_cheads, n, s);
             if (e != hipSuccess) return hip_fail(e, "sa_bwd: dK/dV summing launch");
+        }
+        if (pk.n_groups > 0) {
+            e = combine(pk, true);
+            if (e != hipSuccess) return hip_fail(e, "sa_bwd: dK/dV combining launch");
         }
     }
     if (dqs && !dq_rt) {
         a.items = pq.items;
-        a.heads = ht;
+        a.chunk_tab = pq.chunk_tab;
+        a.partials = pq.partials;
         e = launch_bwd_dq_bf16_t64(d, a, pq.count, false, false, s);
         if (e != hipSuccess) return hip_fail(e, "sa_bwd: dQ kernel launch");
+        if (pq.n_groups > 0) {
+            e = combine(pq, false);
+            if (e != hipSuccess) return hip_fail(e, "sa_bwd: dQ combining launch");
+        }
     }
     return SA_OK;
 }
@@ -634,6 +781,14 @@ int sa_set_fwd_form(int form)
 {
     if (form < 0 || form > 2) return fail(SA_ERR_INVALID_ARG, "sa_set_fwd_form: form %d is not 0, 1 or 2", form);
     return g_fwd_form.exchange(form);
+}
+
+int sa_set_split(int steps, int* previous)
+{
+    if (steps < -1) return fail(SA_ERR_INVALID_ARG, "sa_set_split: steps %d is below -1", steps);
+    const int prev = g_split.exchange(steps);
+    if (previous) *previous = prev;
+    return SA_OK;
 }
 
 const char* sa_status_string(int status)

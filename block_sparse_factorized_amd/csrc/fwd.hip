@@ -79,6 +79,9 @@ __global__ __launch_bounds__(256) void fwd_bf16_t64_kernel(const FwdArgs a)
     const int n32 = lane & 31, hh = lane >> 5;
     const Item item = ld_uniform(&a.items[blockIdx.x]);
     const int bh = item.bh, grp = item.blk;
+    // A chunk of a long list (slot >= 0) walks part of it and leaves partial
+    // results in its slot for the combining pass.
+    const bool chunk = item.slot >= 0;
     const DevLayout L = a.heads.lay[a.heads.head_lay[bh % a.H]];
     const int2 pair = ld_uniform(&L.qgrp_blk[grp]);
     const int qb = member ? pair.y : pair.x;  // -1: this wave has no rows
@@ -88,8 +91,9 @@ __global__ __launch_bounds__(256) void fwd_bf16_t64_kernel(const FwdArgs a)
     // are read clamped (and masked out).
     const int vl = L.vl, vm = L.vm, km = L.km;
     const int rs = vl * D;
-    const int64_t head = (int64_t)bh * a.n * D + (int64_t)item.r * D;
-    const int64_t lrow0 = (int64_t)bh * a.n + item.r;  // lse index of row 0
+    const int res = chunk ? 0 : item.r;
+    const int64_t head = (int64_t)bh * a.n * D + (int64_t)res * D;
+    const int64_t lrow0 = (int64_t)bh * a.n + res;  // lse index of row 0
     const unsigned short* Q = (const unsigned short*)a.q + head;
     const unsigned short* K = (const unsigned short*)a.k + head;
     const unsigned short* V = (const unsigned short*)a.v + head;
@@ -122,8 +126,13 @@ __global__ __launch_bounds__(256) void fwd_bf16_t64_kernel(const FwdArgs a)
 #pragma unroll
         for (int dt = 0; dt < D / 32; ++dt) voff[j4][dt] = TL::tr_off(lane, j4, dt);
 
-    const int p0 = ld_uniform(&L.qgrp_ptr[grp]);
-    const int nblk = ld_uniform(&L.qgrp_ptr[grp + 1]) - p0;
+    int p0 = ld_uniform(&L.qgrp_ptr[grp]);
+    int nblk = ld_uniform(&L.qgrp_ptr[grp + 1]) - p0;
+    if (chunk) {
+        const int2 ct = ld_uniform(&a.chunk_tab[item.slot]);  // {first step, steps}
+        p0 += ct.x;
+        nblk = ct.y;
+    }
 
     f32x16 oacc[D / 32];
 #pragma unroll
@@ -426,6 +435,18 @@ __global__ __launch_bounds__(256) void fwd_bf16_t64_kernel(const FwdArgs a)
 
     if (qb < 0) return;
     const float l_tot = l_run + swap_halves(l_run);
+    if (chunk) {
+        // This chunk's accumulator, row reference and row sum, each register
+        // 64 lanes wide, for the combining pass.
+        float* P = a.partials + (int64_t)item.slot * kFwdSlotFloats(D) + (int64_t)w * ((D / 32) * 16 + 2) * 64 + lane;
+#pragma unroll
+        for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) P[(dt * 16 + i) * 64] = oacc[dt][i];
+        P[((D / 32) * 16) * 64] = m_ref;
+        P[((D / 32) * 16 + 1) * 64] = l_tot;
+        return;
+    }
     if (q_row >= vm) return;  // a ragged block's padding row
     const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
     unsigned short* O = (unsigned short*)a.o + head + (uint32_t)(q_row * rs);
@@ -440,6 +461,76 @@ __global__ __launch_bounds__(256) void fwd_bf16_t64_kernel(const FwdArgs a)
             *(u32x2*)(O + 32 * dt + 8 * g + 4 * hh) = u;
         }
     if (hh == 0) a.lse[lrow0 + (uint32_t)(vl * q_row)] = l_tot > 0.f ? m_ref * a.scale + logf(l_tot) : -INFINITY;
+}
+
+// ---------------------------------------------------------------------------
+// Combining pass of the chunks of long lists.  A chunk c of a row leaves its
+// accumulator O_c = sum_j p_j v_j and row sum l_c, with weights p_j =
+// exp2(c2 s_j - c2 m_c) against its own reference m_c.  With M the largest
+// c2 m_c among the chunks that have weight (l_c > 0), the row's results are
+// those of one pass over the whole list: O = sum_c f_c O_c / sum_c f_c l_c
+// and lse = m* scale + log(sum_c f_c l_c), f_c = exp2(c2 m_c - M), m* the
+// reference that gives M; the chunks are added in list order, so the result
+// does not depend on which chunk ran first.  A row with no weight anywhere
+// gets O = 0, lse = -inf, as in the forward.  Workgroup = one chunked pair,
+// wave and lane as in the forward (wave 2m + wr: rows 32 wr .. of member m).
+template <int D>
+__global__ __launch_bounds__(256) void fwd_combine_kernel(const CombineArgs a)
+{
+    constexpr int T = 64, NR = (D / 32) * 16;
+    const int lane = threadIdx.x & 63;
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int member = w >> 1, wr = w & 1;
+    const int n32 = lane & 31, hh = lane >> 5;
+    const int4 g = ld_uniform(&a.groups[blockIdx.x]);  // {bh, pair, first slot, chunks}
+    const DevLayout L = a.heads.lay[a.heads.head_lay[g.x % a.H]];
+    const int2 pair = ld_uniform(&L.qgrp_blk[g.y]);
+    const int qb = member ? pair.y : pair.x;
+    if (qb < 0) return;
+    const int q_row = qb * T + 32 * wr + n32;
+    if (q_row >= L.vm) return;  // a ragged block's padding row
+    const float c2 = a.scale_log2;
+    const float* P0 = a.partials + (int64_t)g.z * kFwdSlotFloats(D) + (int64_t)w * (NR + 2) * 64 + lane;
+    float mx = -INFINITY, m_best = -INFINITY;
+    for (int c = 0; c < g.w; ++c) {
+        const float* P = P0 + (int64_t)c * kFwdSlotFloats(D);
+        const float m = P[NR * 64], l = P[(NR + 1) * 64];
+        if (l > 0.f && m * c2 > mx) {
+            mx = m * c2;
+            m_best = m;
+        }
+    }
+    f32x16 o[D / 32];
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) o[dt][i] = 0.f;
+    float l_tot = 0.f;
+    for (int c = 0; c < g.w; ++c) {
+        const float* P = P0 + (int64_t)c * kFwdSlotFloats(D);
+        const float l = P[(NR + 1) * 64];
+        if (!(l > 0.f)) continue;
+        const float f = __builtin_amdgcn_exp2f(P[NR * 64] * c2 - mx);
+        l_tot += f * l;
+#pragma unroll
+        for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) o[dt][i] += f * P[(dt * 16 + i) * 64];
+    }
+    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+    const int64_t head = (int64_t)g.x * a.n * D;
+    unsigned short* O = (unsigned short*)a.out0 + head + (uint32_t)(q_row * L.vl * D);
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+        for (int gg = 0; gg < 4; ++gg) {
+            u32x2 u;
+            u[0] = bf16_pair(o[dt][4 * gg + 0] * inv, o[dt][4 * gg + 1] * inv);
+            u[1] = bf16_pair(o[dt][4 * gg + 2] * inv, o[dt][4 * gg + 3] * inv);
+            *(u32x2*)(O + 32 * dt + 8 * gg + 4 * hh) = u;
+        }
+    if (hh == 0)
+        a.lse[(int64_t)g.x * a.n + (uint32_t)(L.vl * q_row)] = l_tot > 0.f ? m_best * a.scale + logf(l_tot) : -INFINITY;
 }
 
 __global__ __launch_bounds__(64) void fwd_f32_t16_d64_kernel(const FwdArgs a)
@@ -547,6 +638,16 @@ hipError_t launch_fwd_bf16_t64(int d, const FwdArgs& a, int n_items, bool paired
         hipLaunchKernelGGL((fwd_bf16_t64_kernel<128, false>), g, b, 0, stream, a);
     return hipGetLastError();
 }
+
+hipError_t launch_fwd_combine_bf16(int d, const CombineArgs& a, int n_groups, hipStream_t stream)
+{
+    if (d == 64)
+        hipLaunchKernelGGL((fwd_combine_kernel<64>), dim3(n_groups), dim3(256), 0, stream, a);
+    else
+        hipLaunchKernelGGL((fwd_combine_kernel<128>), dim3(n_groups), dim3(256), 0, stream, a);
+    return hipGetLastError();
+}
+
 
 hipError_t launch_fwd_f32_t16(int d, const FwdArgs& a, int n_items, hipStream_t stream)
 {

@@ -242,47 +242,61 @@ DevLayout place_layout(const LayoutImage& img, const sa_layout* L, const unsigne
     return v;
 }
 
-void build_work_items(ListKind kind, int32_t B, int32_t H, sa_layout* const* hl, int32_t chunk_steps,
-                      std::vector<Item>* out, DkdvSplit* split)
+void build_work_items(ListKind kind, int32_t B, int32_t H, sa_layout* const* hl, int32_t compact_steps,
+                      int32_t plain_steps, int32_t plain_min, std::vector<Item>* out, Split* split)
 {
     auto listing = [&](const sa_layout* L) -> const std::vector<int32_t>& {
         switch (kind) {
         case kByQuery: return L->row_ptr;
-        case kByQueryPair: return L->qgroups.ptr;
+        case kByQueryPair:
+        case kByQueryPairDq: return L->qgroups.ptr;
         default: return L->kgroups.ptr;
         }
     };
-    // A compact view's key-block pairs are walked in chunks of at most
-    // chunk_steps steps, each with a partial-sum slot, by the dK/dV kernel.
-    const bool chunked = kind == kByKeyPair && chunk_steps > 0;
-    if (split) *split = DkdvSplit();
+    const bool pairs = kind != kByQuery;
+    Split local;
+    Split& sp = split ? *split : local;
+    sp = Split();
     std::vector<Item> items;
     std::vector<int32_t> cost;
+    // One chunk: an item, a slot and its table entry.
+    auto add_chunk = [&](int32_t bh, int32_t blk, int32_t first, int32_t steps) {
+        const int32_t slot = (int32_t)sp.slots++;
+        sp.chunk_tab.push_back(make_int2(first, steps));
+        items.push_back(Item{bh, blk, 0, slot});
+        cost.push_back(steps);
+    };
     for (int32_t bh = 0; bh < B * H; ++bh) {
         const sa_layout* L = hl[bh % H];
         const std::vector<int32_t>& ptr = listing(L);
-        if (chunked && is_compact(L)) {
-            if (split) split->heads.push_back(make_int2(bh, (int32_t)split->groups.size()));
+        if (kind == kByKeyPair && compact_steps > 0 && is_compact(L)) {
+            // every key-block pair of a compact view, in chunks of compact_steps
+            sp.cheads.push_back(make_int2(bh, (int32_t)sp.cgroups.size()));
             for (int64_t blk = 0; blk + 1 < (int64_t)ptr.size(); ++blk) {
                 const int32_t len = ptr[blk + 1] - ptr[blk];
-                const int32_t chunks = std::max<int32_t>(1, (len + chunk_steps - 1) / chunk_steps);
-                const int32_t first = split ? (int32_t)split->slots : 0;
-                for (int32_t c = 0; c < chunks; ++c) {
-                    items.push_back(Item{bh, (int32_t)blk, c * chunk_steps, first + c});
-                    cost.push_back(std::min(chunk_steps, len - c * chunk_steps));
-                }
-                if (split) {
-                    split->groups.push_back(make_int2(first, chunks));
-                    split->slots += chunks;
-                }
+                const int32_t chunks = std::max<int32_t>(1, (len + compact_steps - 1) / compact_steps);
+                sp.cgroups.push_back(make_int2((int32_t)sp.slots, chunks));
+                for (int32_t c = 0; c < chunks; ++c)
+                    add_chunk(bh, (int32_t)blk, c * compact_steps, std::min(compact_steps, len - c * compact_steps));
             }
             continue;
         }
         // (a residue view walks its dense causal layout once per residue class)
         for (int64_t r = 0; r < L->view_l; ++r)
             for (int64_t blk = 0; blk + 1 < (int64_t)ptr.size(); ++blk) {
+                const int32_t len = ptr[blk + 1] - ptr[blk];
+                if (pairs && plain_steps > 0 && L->view_l == 1 && len > std::max(plain_min, plain_steps)) {
+                    // near-equal chunks: chunk c walks steps [c*len/k, (c+1)*len/k)
+                    const int32_t k = (len + plain_steps - 1) / plain_steps;
+                    sp.groups.push_back(make_int4(bh, (int32_t)blk, (int32_t)sp.slots, k));
+                    for (int32_t c = 0; c < k; ++c) {
+                        const int32_t f0 = (int32_t)((int64_t)c * len / k), f1 = (int32_t)((int64_t)(c + 1) * len / k);
+                        add_chunk(bh, (int32_t)blk, f0, f1 - f0);
+                    }
+                    continue;
+                }
                 items.push_back(Item{bh, (int32_t)blk, (int32_t)r, -1});
-                cost.push_back(ptr[blk + 1] - ptr[blk]);
+                cost.push_back(len);
             }
     }
     std::vector<size_t> order(items.size());

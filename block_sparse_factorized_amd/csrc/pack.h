@@ -32,28 +32,40 @@ int pack_layout(sa_layout* L, LayoutImage* img);
 DevLayout place_layout(const LayoutImage& img, const sa_layout* L, const unsigned char* base);
 
 // What a work list's items walk: query blocks (fp32 forward), query-block
-// pairs (bf16 forward, dQ) or key-block pairs (dK/dV).
-enum ListKind { kByQuery = 0, kByQueryPair = 1, kByKeyPair = 2 };
+// pairs (bf16 forward; dQ, a list of its own since its chunks differ) or
+// key-block pairs (dK/dV).
+enum ListKind { kByQuery = 0, kByQueryPair = 1, kByKeyPair = 2, kByQueryPairDq = 3 };
 
 // A compact view of fixed B (its keys are the summary positions).
 inline bool is_compact(const sa_layout* L) { return L->key_gl != 0; }
 
-// What the dK/dV kernel's chunks of compact views write and the summing
-// pass reads (see ReduceArgs): per compact (batch, head) {bh, offset into
-// groups}; per key-block pair {first slot, chunks}; the number of slots.
-struct DkdvSplit {
-    std::vector<int2> heads;
-    std::vector<int2> groups;
+// The chunks of a work list's long lists and what their combining passes
+// read.  Every chunk has a slot: chunk_tab[slot] = {first step, steps} of
+// its part of the list, and the kernel leaves its partial results in that
+// slot.  groups: each chunked list of a layout walked as itself (not a
+// compact view), {bh, pair index, first slot, chunks}, for the combining
+// pass of its kernel.  cheads / cgroups: the dK/dV summing pass of compact
+// views (see ReduceArgs): per compact (batch, head) {bh, offset into
+// cgroups}; per key-block pair {first slot, chunks}.
+struct Split {
+    std::vector<int2> chunk_tab;
+    std::vector<int4> groups;
+    std::vector<int2> cheads;
+    std::vector<int2> cgroups;
     int64_t slots = 0;
 };
 
 // The work items of a call over B batches and H heads (layout hl[h] for
 // head h): one per (batch*head, block or pair, residue class), longest list
 // first, so the heaviest items start early and the tail is made of short
-// ones.  With kind kByKeyPair and chunk_steps > 0, compact views' key-block
-// pairs become one item per chunk of at most chunk_steps steps of their
-// query lists, and split (if not null) receives their slots.
-void build_work_items(ListKind kind, int32_t B, int32_t H, sa_layout* const* hl, int32_t chunk_steps,
-                      std::vector<Item>* out, DkdvSplit* split = nullptr);
+// ones.  Chunking (the pair kinds; residue views never):
+//   compact_steps > 0 (kByKeyPair): every key-block pair of a compact view
+//     is walked in chunks of at most compact_steps steps, in list order;
+//   plain_steps > 0: a list of any other layout longer than both plain_min
+//     and plain_steps steps is cut into ceil(len / plain_steps) chunks of
+//     near-equal length.
+// split (if not null) receives the chunks' description.
+void build_work_items(ListKind kind, int32_t B, int32_t H, sa_layout* const* hl, int32_t compact_steps,
+                      int32_t plain_steps, int32_t plain_min, std::vector<Item>* out, Split* split = nullptr);
 
 }  // namespace sa

@@ -216,7 +216,15 @@ void sa_layout_destroy(sa_layout_t* lay);
  * Errors: SA_ERR_INVALID_ARG for NULL/misaligned pointers, B < 1, H < 1,
  * H > 256, a layout whose n differs, a bad scale, more than 8 distinct
  * layouts; SA_ERR_UNSUPPORTED for a (dtype, block, d) not compiled;
- * SA_ERR_HIP if a HIP call or the launch fails.
+ * SA_ERR_HIP if a HIP call or the launch fails; SA_ERR_ALLOC when memory
+ * for the work list runs out.  One kernel, or two when long lists are
+ * walked in chunks (sa_set_split).  The work list of (head_layout, B, H, d)
+ * is built and kept on the device on the first call, with a partial-result
+ * buffer per stream that runs it; calls on different streams may overlap.
+ * Under graph capture nothing is allocated: a stream being captured that
+ * has no buffer of its own uses one made for another stream by an earlier
+ * uncaptured call (SA_ERR_UNSUPPORTED if there is none), and the captured
+ * work must not overlap that stream's calls.
  */
 int sa_fwd(const sa_layout_t* const* head_layout, int32_t B, int32_t H, int64_t n, int32_t d,
            int dtype, float scale, const void* q, const void* k, const void* v, void* o,
@@ -243,8 +251,9 @@ size_t sa_bwd_workspace_size(int32_t B, int32_t H, int64_t n, int32_t d);
  * caller, contents ignored on entry.  Same errors as sa_fwd, plus
  * SA_ERR_INVALID_ARG when ws_bytes is too small.  Deterministic: no atomics,
  * so equal inputs give bitwise equal outputs.  Runs sa_bwd_dq_rowterms then
- * sa_bwd_dkdv (two kernels; three with compact views, whose dK/dV chunks are
- * summed by a third).
+ * sa_bwd_dkdv: two kernels, and a combining kernel after each whose long
+ * lists are walked in chunks (sa_set_split) or, for dK/dV, after a compact
+ * view's chunks.  Partial results are kept per stream, as for sa_fwd.
  */
 int sa_bwd(const sa_layout_t* const* head_layout, int32_t B, int32_t H, int64_t n, int32_t d,
            int dtype, float scale, const void* q, const void* k, const void* v, const void* o,
@@ -266,8 +275,10 @@ int sa_bwd(const sa_layout_t* const* head_layout, int32_t B, int32_t H, int64_t 
  * different streams, or from several threads without ordering) race and
  * give wrong gradients; calls ordered on one stream are safe.  The scratch
  * needs no clearing (the first kernel writes every row term the second
- * reads).  Compact views' dK/dV partial sums use the buffer cached with the
- * work list (made by that earlier sa_bwd), under the same rule.
+ * reads).  The chunks' partial results (sa_set_split, compact views) use a
+ * buffer cached with the work list: the one made for this stream by an
+ * earlier sa_bwd, else the one made for another stream, under the same
+ * rule.
  */
 int sa_bwd_noalloc(const sa_layout_t* const* head_layout, int32_t B, int32_t H, int64_t n, int32_t d,
                    int dtype, float scale, const void* q, const void* k, const void* v, const void* o,
@@ -321,6 +332,37 @@ int sa_bwd_dq(const sa_layout_t* const* head_layout, int32_t B, int32_t H, int64
  * value.  Calls of sa_fwd that are already enqueued are not affected.
  */
 int sa_set_fwd_form(int form);
+
+/*
+ * Chunking of long lists, process-wide: a tuning and testing switch.  The
+ * bf16 forward, dQ and dK/dV kernels run one workgroup per pair of blocks,
+ * longest list first, and the workgroups of a compute unit share its
+ * SIMDs, so a unit's time follows the steps it is given.  When one pair's
+ * list is longer than whole units' loads (a batch of one and few heads)
+ * that list would set the launch's end while other units idle; such a list
+ * is walked in chunks by several workgroups, each leaving fp32 partial
+ * results in a device buffer the library keeps with the call's work list
+ * (one per stream that runs it), and a combining kernel adds each list's
+ * chunks in list order and writes the pair's rows: the forward's chunks
+ * carry their running reference and row sum, and are rescaled to the
+ * largest reference before they are added, as the online softmax does
+ * between key blocks ("OpenAI Sparse Transformer", "Implementation and
+ * Limitations": the kernels split the work by blocks).  Results are
+ * deterministic (fixed order, no atomics) and equal to those of an
+ * unchunked walk up to rounding order.  Residue views are never chunked;
+ * compact views' dK/dV chunks (96 steps) are not affected.
+ *   0   chosen per call (default): lists longer than twice the average
+ *       number of steps per compute unit (at least 16) are cut into chunks
+ *       of that length; calls whose every unit holds many lists' worth of
+ *       steps get no chunks
+ *   -1  no chunks
+ *   k>0 every list longer than k steps in ceil(len / k) near-equal chunks
+ * *previous (if not NULL) receives the setting before the call.  Returns
+ * SA_OK, or SA_ERR_INVALID_ARG (setting unchanged) for a value below -1.
+ * Work lists built before the change keep their chunks; later calls use
+ * lists built under the new setting.
+ */
+int sa_set_split(int steps, int* previous);
 
 /* Static text of a status code. */
 const char* sa_status_string(int status);

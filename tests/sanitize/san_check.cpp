@@ -68,42 +68,86 @@ void check_image(sa_layout* L, const char* what)
                 CHECK(st[x].z >= -2 && st[x].z < L->n_masks, "%s: mask b %d", what, st[x].z);
             }
     }
-    for (ListKind kind : {kByQuery, kByQueryPair, kByKeyPair})
+    for (ListKind kind : {kByQuery, kByQueryPair, kByKeyPair, kByQueryPairDq})
         for (int32_t B : {1, 3}) {
             sa_layout* hl[2] = {L, L};
             std::vector<Item> items;
-            build_work_items(kind, B, 2, hl, 0, &items);
+            build_work_items(kind, B, 2, hl, 0, 0, 0, &items);
             const size_t per = kind == kByQuery ? L->row_ptr.size() - 1
-                               : kind == kByQueryPair ? L->qgroups.ptr.size() - 1
-                                                      : L->kgroups.ptr.size() - 1;
+                               : kind == kByKeyPair ? L->kgroups.ptr.size() - 1
+                                                    : L->qgroups.ptr.size() - 1;
             CHECK(items.size() == (size_t)B * 2 * per * (size_t)L->view_l, "%s: %zu items", what, items.size());
             for (const Item& it : items)
                 CHECK(it.bh >= 0 && it.bh < B * 2 && it.blk >= 0 && (size_t)it.blk < per && it.r >= 0 &&
-                          it.r < L->view_l,
+                          it.r < L->view_l && it.slot == -1,
                       "%s: item", what);
         }
-    // A compact view's dK/dV list in chunks: every chunk inside its pair's
-    // list, the chunks of a pair covering it exactly, slots distinct.
-    if (is_compact(L))
+    // Chunked lists: every chunk inside its list, the chunks of a list
+    // covering it exactly and in order, slots distinct and each named by
+    // one item, the tables consistent.  Compact views' dK/dV lists in chunks
+    // of compact_steps; other layouts' lists (not residue views) longer than
+    // the threshold in near-equal chunks of at most plain_steps.
+    for (ListKind kind : {kByQueryPair, kByKeyPair, kByQueryPairDq})
         for (int32_t steps : {1, 7, 64}) {
             sa_layout* hl[2] = {L, L};
             std::vector<Item> items;
-            DkdvSplit split;
-            build_work_items(kByKeyPair, 2, 2, hl, steps, &items, &split);
-            const size_t ng = L->kgroups.ptr.size() - 1;
-            CHECK(split.heads.size() == 4 && split.groups.size() == 4 * ng, "%s: split tables", what);
-            std::vector<int> seen((size_t)split.slots, 0);
+            Split sp;
+            const int32_t cst = kind == kByKeyPair ? steps : 0;
+            const int32_t pmin = steps == 1 ? 3 : steps;
+            build_work_items(kind, 2, 2, hl, cst, steps, pmin, &items, &sp);
+            const std::vector<int32_t>& ptr = kind == kByKeyPair ? L->kgroups.ptr : L->qgroups.ptr;
+            const size_t ng = ptr.size() - 1;
+            const bool compact = kind == kByKeyPair && is_compact(L);
+            CHECK((int64_t)sp.chunk_tab.size() == sp.slots, "%s: chunk table", what);
+            if (compact) CHECK(sp.cheads.size() == 4 && sp.cgroups.size() == 4 * ng && sp.groups.empty(), "%s: compact tables", what);
+            else CHECK(sp.cheads.empty() && sp.cgroups.empty(), "%s: no compact tables", what);
+            if (L->view_l > 1) CHECK(sp.slots == 0, "%s: residue views are not chunked", what);
+            std::vector<int> seen((size_t)sp.slots, 0);
+            size_t plain_items = 0;
             for (const Item& it : items) {
-                CHECK(it.slot >= 0 && it.slot < split.slots && it.blk >= 0 && (size_t)it.blk < ng, "%s: chunk", what);
-                if (it.slot < 0 || it.slot >= split.slots || it.blk < 0 || (size_t)it.blk >= ng) continue;
+                CHECK(it.blk >= 0 && (size_t)it.blk < ng, "%s: item block", what);
+                if (it.slot < 0) {
+                    ++plain_items;
+                    const int32_t len = ptr[it.blk + 1] - ptr[it.blk];
+                    CHECK(compact == false && (L->view_l > 1 || len <= std::max(pmin, steps)), "%s: unchunked long list", what);
+                    continue;
+                }
+                CHECK(it.slot < sp.slots && it.r == 0, "%s: chunk item", what);
+                if (it.slot >= sp.slots) continue;
                 ++seen[(size_t)it.slot];
-                const int32_t len = L->kgroups.ptr[it.blk + 1] - L->kgroups.ptr[it.blk];
-                const int2 gs = split.groups[(size_t)split.heads[(size_t)it.bh].y + (size_t)it.blk];
-                CHECK(split.heads[(size_t)it.bh].x == it.bh, "%s: head table", what);
-                CHECK(it.r == (it.slot - gs.x) * steps && (it.r < len || (len == 0 && it.r == 0)), "%s: chunk start", what);
-                CHECK(gs.y == std::max<int32_t>(1, (len + steps - 1) / steps), "%s: chunk count", what);
             }
             for (int x : seen) CHECK(x == 1, "%s: slot used %d times", what, x);
+            // every list's chunks, through its table entry
+            auto cover = [&](int32_t blk, int32_t first, int32_t chunks, int32_t cap, bool equal) {
+                const int32_t len = ptr[blk + 1] - ptr[blk];
+                int32_t at = 0, lo = INT32_MAX, hi = 0;
+                for (int32_t c = 0; c < chunks; ++c) {
+                    CHECK(first + c < sp.slots, "%s: chunk slot", what);
+                    if (first + c >= sp.slots) return;
+                    const int2 ct = sp.chunk_tab[(size_t)(first + c)];
+                    CHECK(ct.x == at && ct.y >= 0 && ct.y <= cap, "%s: chunk %d of list %d: {%d, %d} at %d", what, c, blk, ct.x, ct.y, at);
+                    at += ct.y;
+                    lo = std::min(lo, ct.y);
+                    hi = std::max(hi, ct.y);
+                }
+                CHECK(at == len, "%s: chunks cover %d of %d steps", what, at, len);
+                if (equal) CHECK(chunks >= 2 && hi - lo <= 1, "%s: chunks not near-equal", what);
+            };
+            for (const int2& h : sp.cheads)
+                for (size_t gi = 0; gi < ng; ++gi) {
+                    const int2 gs = sp.cgroups[(size_t)h.y + gi];
+                    const int32_t len = ptr[gi + 1] - ptr[gi];
+                    CHECK(gs.y == std::max<int32_t>(1, (len + steps - 1) / steps), "%s: chunk count", what);
+                    cover((int32_t)gi, gs.x, gs.y, steps, false);
+                }
+            for (const int4& g : sp.groups) {
+                CHECK(g.x >= 0 && g.x < 4 && g.y >= 0 && (size_t)g.y < ng, "%s: group", what);
+                if (g.y < 0 || (size_t)g.y >= ng) continue;
+                const int32_t len = ptr[g.y + 1] - ptr[g.y];
+                CHECK(len > std::max(pmin, steps) && g.w == (len + steps - 1) / steps, "%s: group chunks", what);
+                cover(g.y, g.z, g.w, steps, true);
+            }
+            CHECK(plain_items + (size_t)sp.slots == items.size(), "%s: item count", what);
         }
 }
 

@@ -252,6 +252,20 @@ def fwd_form():
         sa.sa_set_fwd_form(forms[0])
 
 
+@pytest.fixture
+def split_steps():
+    """Forces the chunking of long lists (sa_set_split) for one test, then
+    restores the automatic choice."""
+    prev = []
+
+    def force(steps):
+        prev.append(sa.sa_set_split(steps))
+
+    yield force
+    if prev:
+        sa.sa_set_split(prev[0])
+
+
 def _ramp_inputs(kind, n, d, seed):
     """Q rows along one direction u and K rows placed along u by a per-key
     ramp, so scores follow the ramp: "rising" puts every row's max at its
@@ -724,11 +738,15 @@ def test_destroy_releases_work_lists():
     assert free_after >= free_before - (8 << 20), (free_before - free_after)
 
 
-def test_graph_capture_replays():
+@pytest.mark.parametrize("steps", [0, 3])
+def test_graph_capture_replays(steps, split_steps):
     """After one uncaptured call (which uploads the layouts and work lists),
     sa_fwd + sa_bwd only enqueue kernels: captured into a graph and replayed
     several times, with eager work between the replays, every replay gives
-    the eager results bit for bit."""
+    the eager results bit for bit.  steps = 3: long lists in chunks, so the
+    capture also holds the combining kernels and uses the partial-result
+    buffer made by the uncaptured call (another stream's)."""
+    split_steps(steps)
     n = 1024
     pats = [("strided_a", 128, 1), ("strided_b", 128, 1), ("fixed_a", 128, 32), ("fixed_b", 128, 32)]
     x = workloads.custom_inputs((2, 4, n, 64), torch.bfloat16, seed=31)
@@ -760,6 +778,126 @@ def test_graph_capture_replays():
             assert torch.equal(got, want), (rep, nm)
         sa.sa_fwd(q, k, v, lays, 1.0)  # eager work between replays
         torch.cuda.synchronize()
+
+
+# ---------------------------------------------------------------------------
+# Long lists walked in chunks (sa_set_split): partial results combined in
+# list order by a second kernel per stage.
+
+SPLIT = [
+    # (head patterns, n, d, views, note)
+    ([("strided_a", 128, 1), ("strided_b", 128, 1)], 2048, 64, False, "strided heads"),
+    ([("fixed_a", 128, 32), ("fixed_b", 128, 32)], 2048, 64, False, "fixed heads: empty first rows"),
+    ([("strided_b", 64, 1), ("dense", 1, 1)], 1024, 128, False, "d = 128, dense head"),
+    ([("fixed_b", 128, 32), ("strided_b", 128, 1), ("strided_a", 96, 1)], 1920, 64, True,
+     "compact and residue views beside a plain head, ragged last blocks"),
+]
+
+
+@pytest.mark.parametrize("steps", [1, 5])
+@pytest.mark.parametrize("form", ["half", "paired"])
+@pytest.mark.parametrize("case", SPLIT, ids=[c[4] for c in SPLIT])
+def test_chunked_lists_match_oracle(case, form, steps, split_steps, fwd_form):
+    """Every list longer than `steps` is walked in chunks of at most `steps`
+    (one step each: a chunk often holds no allowed key of a row, whose
+    partial row sum is then zero); both forward forms; against the oracle,
+    every head whole with the elementwise bound."""
+    pats, n, d, views, _ = case
+    split_steps(steps)
+    fwd_form(form)
+    H = len(pats)
+    x = workloads.custom_inputs((2, H, n, d), torch.bfloat16, seed=7 * n + d + steps)
+    lays = view_layouts(pats, n) if views else layouts_for(pats, n, 64)
+    res = run(x, pats, 64, 1.0, backward=True, lays=lays)
+    for b in range(2):
+        for h in range(H):
+            compare_head(x, res, b, h, pats[h], 1.0, True, fp32=False)
+
+
+def test_chunked_lists_agree_with_unchunked(split_steps):
+    """The same call with and without chunks: equal up to rounding order
+    (bf16 outputs within a few units of the last place)."""
+    pats, n, d = [("strided_a", 128, 1), ("strided_b", 128, 1), ("fixed_b", 128, 32)], 2048, 64
+    x = workloads.custom_inputs((2, 3, n, d), torch.bfloat16, seed=404)
+    split_steps(-1)
+    r0 = run(x, pats, 64, 1.0, backward=True)
+    sa.sa_set_split(3)
+    r1 = run(x, pats, 64, 1.0, backward=True)
+    for t in ("o", "dq", "dk", "dv"):
+        a, b = r0[t].float(), r1[t].float()
+        assert torch.allclose(a, b, rtol=2e-2, atol=2e-3), (t, (a - b).abs().max().item())
+    fin = torch.isfinite(r0["lse"])
+    assert torch.equal(fin, torch.isfinite(r1["lse"]))
+    assert (r0["lse"][fin] - r1["lse"][fin]).abs().max().item() <= 1e-4
+
+
+def test_chunked_bitwise_repeat_and_every_output_written(split_steps):
+    """Chunks combined in a fixed order: two runs agree bit for bit, also
+    with NaN-filled outputs (every element of O, lse, dQ, dK, dV written)."""
+    split_steps(4)
+    pats, n, d = [("strided_b", 128, 1), ("fixed_b", 64, 16)], 1472, 64
+    x = workloads.custom_inputs((2, 2, n, d), torch.bfloat16, seed=77)
+    lays = layouts_for(pats, n, 64)
+    q, k, v, do = (x[t].to(DEV) for t in ("q", "k", "v", "do"))
+    ref_o, ref_lse = sa.sa_fwd(q, k, v, lays, 1.0)
+    ref = sa.sa_bwd(q, k, v, ref_o, ref_lse, do, lays, 1.0)
+    nan = float("nan")
+    o = torch.full_like(q, nan)
+    lse = torch.full(q.shape[:3], nan, dtype=torch.float32, device=DEV)
+    sa.sa_fwd(q, k, v, lays, 1.0, o=o, lse=lse)
+    dq, dk, dv = (torch.full_like(q, nan) for _ in range(3))
+    sa.sa_bwd(q, k, v, o, lse, do, lays, 1.0, dq=dq, dk=dk, dv=dv)
+    torch.cuda.synchronize()
+    assert torch.equal(o, ref_o) and torch.equal(lse, ref_lse)
+    for got, want, nm in zip((dq, dk, dv), ref, ("dq", "dk", "dv")):
+        assert not torch.isnan(got.float()).any(), nm
+        assert torch.equal(got, want), nm
+
+
+def test_auto_chunks_underfilled_call(split_steps):
+    """A batch of one with two heads leaves most compute units without a
+    list of their own: the per-call rule (sa_set_split(0)) cuts the long
+    lists into chunks.  Sampled rows and key columns against the oracle,
+    and the results differ from the unchunked run in rounding (so chunks
+    were taken)."""
+    pats, n, d = [("strided_a", 128, 1), ("strided_b", 128, 1)], 8192, 64
+    x = workloads.custom_inputs((1, 2, n, d), torch.bfloat16, seed=8192)
+    split_steps(0)
+    lays = layouts_for(pats, n, 64)
+    res = run(x, pats, 64, 1.0, backward=True, lays=lays)
+    rows = sorted(set(list(range(0, 64)) + list(range(4032, 4160)) + list(range(n - 96, n))))
+    for h in range(2):
+        compare_head(x, res, 0, h, pats[h], 1.0, True, fp32=False, rows=rows)
+    sa.sa_set_split(-1)
+    ref = run(x, pats, 64, 1.0, backward=True, lays=layouts_for(pats, n, 64))
+    assert any(not torch.equal(res[t], ref[t]) for t in ("o", "dq", "dk", "dv"))
+
+
+def test_chunked_calls_on_two_streams(split_steps):
+    """Chunked calls on two streams at once use separate partial buffers:
+    each stream's results equal the same call run alone."""
+    split_steps(2)
+    pats, n, d = [("strided_a", 128, 1), ("strided_b", 128, 1)], 2048, 64
+    lays = layouts_for(pats, n, 64)
+    xs = [workloads.custom_inputs((2, 2, n, d), torch.bfloat16, seed=s) for s in (5, 6)]
+    dev = [{t: x[t].to(DEV) for t in ("q", "k", "v", "do")} for x in xs]
+    refs = []
+    for dd in dev:
+        o, lse = sa.sa_fwd(dd["q"], dd["k"], dd["v"], lays, 1.0)
+        refs.append((o, lse) + tuple(sa.sa_bwd(dd["q"], dd["k"], dd["v"], o, lse, dd["do"], lays, 1.0)))
+    torch.cuda.synchronize()
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    outs = [None, None]
+    for rep in range(3):
+        for i, (st, dd) in enumerate(zip(streams, dev)):
+            st.wait_stream(torch.cuda.current_stream())
+            with torch.cuda.stream(st):
+                o, lse = sa.sa_fwd(dd["q"], dd["k"], dd["v"], lays, 1.0)
+                outs[i] = (o, lse) + tuple(sa.sa_bwd(dd["q"], dd["k"], dd["v"], o, lse, dd["do"], lays, 1.0))
+        torch.cuda.synchronize()
+        for i in range(2):
+            for got, want, nm in zip(outs[i], refs[i], ("o", "lse", "dq", "dk", "dv")):
+                assert torch.equal(got, want), (rep, i, nm)
 
 
 # ---------------------------------------------------------------------------

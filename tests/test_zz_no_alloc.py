@@ -21,7 +21,23 @@ CALLS = [
 ]
 
 
-def test_noalloc_matches_sa_bwd_on_two_calls():
+@pytest.fixture
+def split_steps():
+    prev = []
+
+    def force(steps):
+        prev.append(sa.sa_set_split(steps))
+
+    yield force
+    if prev:
+        sa.sa_set_split(prev[0])
+
+
+@pytest.mark.parametrize("steps", [0, 3])
+def test_noalloc_matches_sa_bwd_on_two_calls(steps, split_steps):
+    """steps = 3: long lists in chunks, whose partial results go to the
+    buffer the earlier sa_bwd made (no allocation either)."""
+    split_steps(steps)
     free_seen = []
     for (B, H, n, d, pats, seed) in CALLS:
         lays = [sa.sa_layout_build(p, n, l, c, block=64) for (p, l, c) in pats]
