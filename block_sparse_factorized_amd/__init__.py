@@ -36,6 +36,7 @@ from ._binding import (  # noqa: F401
     sa_layout_set_residue_view,
     sa_layout_view_info,
     sa_set_fwd_form,
+    sa_set_one_paths,
     sa_set_split,
     sparse_attention,
 )

@@ -36,7 +36,7 @@ EXPORTED = [
     "sa_layout_build", "sa_layout_info", "sa_layout_export", "sa_layout_set_residue_view",
     "sa_layout_set_compact_view", "sa_layout_view_info", "sa_layout_destroy",
     "sa_fwd", "sa_bwd", "sa_bwd_workspace_size", "sa_bwd_dq_rowterms", "sa_bwd_rowterms", "sa_bwd_dkdv",
-    "sa_bwd_dq", "sa_bwd_noalloc", "sa_set_fwd_form", "sa_set_split",
+    "sa_bwd_dq", "sa_bwd_noalloc", "sa_set_fwd_form", "sa_set_split", "sa_set_one_paths",
     "sa_status_string", "sa_last_error",
 ]
 
@@ -88,6 +88,8 @@ def _load():
     lib.sa_set_fwd_form.restype = cint
     lib.sa_set_split.argtypes = [cint, ctypes.POINTER(cint)]
     lib.sa_set_split.restype = cint
+    lib.sa_set_one_paths.argtypes = [cint, ctypes.POINTER(cint)]
+    lib.sa_set_one_paths.restype = cint
     lib.sa_status_string.argtypes = [cint]
     lib.sa_status_string.restype = ctypes.c_char_p
     lib.sa_last_error.argtypes = []
@@ -199,6 +201,14 @@ def sa_set_split(steps: int) -> int:
     prev = ctypes.c_int()
     _check(_lib.sa_set_split(int(steps), ctypes.byref(prev)))
     return prev.value
+
+
+def sa_set_one_paths(enable: bool) -> bool:
+    """Process-wide switch of the one-exponential paths (see
+    sa_set_one_paths in sa.h).  Returns the previous setting."""
+    prev = ctypes.c_int()
+    _check(_lib.sa_set_one_paths(int(bool(enable)), ctypes.byref(prev)))
+    return bool(prev.value)
 
 
 def sa_layout_build(pattern: Union[str, int], n: int, l: int, c: int = 1, block: int = 64) -> Layout:

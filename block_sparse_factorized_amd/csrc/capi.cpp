@@ -21,6 +21,8 @@ namespace sa {
 namespace {
 // sa_set_fwd_form: 0 chosen per call, 1 per-half form, 2 two-half form.
 std::atomic<int> g_fwd_form{0};
+// sa_set_one_paths: 1 the one-exponential paths are used, 0 never.
+std::atomic<int> g_one_paths{1};
 }
 
 namespace {
@@ -506,6 +508,7 @@ int sa_fwd(const sa_layout_t* const* head_layout, int32_t B, int32_t H, int64_t 
     a.heads = ht;
     a.chunk_tab = plan.chunk_tab;
     a.partials = plan.partials;
+    a.one_bits = g_one_paths.load(std::memory_order_relaxed) ? 3u : 0u;
     // The paired form when most of the walk's wave-steps have both halves
     // live (full blocks: dense layouts, residue views, wide strided A).  A
     // residue view's layout is walked once per residue class, view_l times
@@ -635,6 +638,7 @@ int bwd_call(const char* fn, int stages, const sa_layout_t* const* head_layout, 
     // (strided B); elsewhere the plain form keeps its grouped operand reads.
     bool one = false;
     for (int x = 0; x < nl; ++x) one = one || distinct[x]->one_quads;
+    if (!g_one_paths.load(std::memory_order_relaxed)) one = false;
     if (dq_rt) {
         a.items = pq.items;
         a.chunk_tab = pq.chunk_tab;
@@ -781,6 +785,14 @@ int sa_set_fwd_form(int form)
 {
     if (form < 0 || form > 2) return fail(SA_ERR_INVALID_ARG, "sa_set_fwd_form: form %d is not 0, 1 or 2", form);
     return g_fwd_form.exchange(form);
+}
+
+int sa_set_one_paths(int enable, int* previous)
+{
+    if (enable != 0 && enable != 1) return fail(SA_ERR_INVALID_ARG, "sa_set_one_paths: enable %d is not 0 or 1", enable);
+    const int prev = g_one_paths.exchange(enable);
+    if (previous) *previous = prev;
+    return SA_OK;
 }
 
 int sa_set_split(int steps, int* previous)

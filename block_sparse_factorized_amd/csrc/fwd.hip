@@ -198,7 +198,7 @@ __global__ __launch_bounds__(256) void fwd_bf16_t64_kernel(const FwdArgs a)
             // masks are not applied.
             const unsigned fl = ((unsigned)step.w >> (8 + 4 * member + 2 * wr)) & 3u;
             // Bit kt of o1: each lane has at most one allowed element in half kt.
-            const unsigned o1 = ((unsigned)step.w >> (16 + 4 * member + 2 * wr)) & 3u;
+            const unsigned o1 = ((unsigned)step.w >> (16 + 4 * member + 2 * wr)) & a.one_bits;
 
             if constexpr (PAIRED) {
                 // Both halves of the step together: their score products

@@ -51,6 +51,8 @@ struct FwdArgs {
     // partial results, kFwdSlotFloats(D) floats per slot (see fwd.hip).
     const int2* chunk_tab;
     float* partials;
+    // 3: one-element halves take the one-exponential path; 0: never.
+    uint32_t one_bits;
 };
 
 struct BwdArgs {

@@ -364,6 +364,22 @@ int sa_set_fwd_form(int form);
  */
 int sa_set_split(int steps, int* previous);
 
+/*
+ * One-exponential paths, process-wide: a testing and comparison switch.
+ * Where a 32 x 32 quadrant of a block leaves each lane of the forward's
+ * (and dQ's) tile at most one allowed element -- strided B's diagonal
+ * blocks, fixed B with one summary column -- those kernels take that
+ * element alone: one exponential per lane instead of sixteen, its weight
+ * placed back into the tile (the dK/dV kernel, whose lanes are keys, has no
+ * such path: there the selection chains cost more than the exponentials
+ * they save).  enable = 1 (default) takes them where the quadrants allow,
+ * 0 never; both give the same results up to rounding.  *previous (if not
+ * NULL) receives the setting before the call.  Returns SA_OK, or
+ * SA_ERR_INVALID_ARG (setting unchanged) for another value.  Calls already
+ * enqueued are not affected.
+ */
+int sa_set_one_paths(int enable, int* previous);
+
 /* Static text of a status code. */
 const char* sa_status_string(int status);
 

@@ -363,6 +363,44 @@ def test_one_element_quadrants(d):
             compare_head(x, res, b, h, pats[h], 1.0 / math.sqrt(d), True, fp32=False)
 
 
+@pytest.fixture
+def one_paths():
+    """Switches the one-exponential paths for one test, then restores them."""
+    prev = []
+
+    def force(enable):
+        prev.append(sa.sa_set_one_paths(enable))
+
+    yield force
+    if prev:
+        sa.sa_set_one_paths(prev[0])
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_one_paths_match_general_paths(d, one_paths):
+    """The same calls with the forward's and dQ's one-exponential paths on
+    and off: O and dQ agree to rounding, dK and dV bit for bit (the dK/dV
+    kernel has one path; the row terms the dQ kernel forms for it are the
+    same either way), and both runs match the oracle.  Strided B at 128 and
+    256 (diagonal blocks in every list) beside strided A and fixed B with
+    one summary column."""
+    n = 2048
+    pats = [("strided_b", 128, 1), ("strided_a", 128, 1), ("strided_b", 256, 1), ("fixed_b", 64, 1)]
+    x = workloads.custom_inputs((2, len(pats), n, d), torch.bfloat16, seed=90 + d)
+    lays = layouts_for(pats, n, 64)
+    one_paths(True)
+    r1 = run(x, pats, 64, 1.0 / math.sqrt(d), backward=True, lays=lays)
+    sa.sa_set_one_paths(False)
+    r0 = run(x, pats, 64, 1.0 / math.sqrt(d), backward=True, lays=lays)
+    assert torch.equal(r1["dk"], r0["dk"]) and torch.equal(r1["dv"], r0["dv"])
+    for t in ("o", "dq"):
+        assert torch.allclose(r1[t].float(), r0[t].float(), rtol=2e-2, atol=2e-3), t
+    for res in (r1, r0):
+        for b in range(2):
+            for h in range(len(pats)):
+                compare_head(x, res, b, h, pats[h], 1.0 / math.sqrt(d), True, fp32=False)
+
+
 def test_fp32_tiny_variants():
     for pats, n in (([("fixed_a", 32, 1), ("fixed_b", 32, 8)], 256), ([("strided_a", 20, 1), ("dense", 1, 1)], 160)):
         x = workloads.custom_inputs((2, 2, n, 64), torch.float32, seed=n, with_dout=False)
