@@ -47,6 +47,11 @@ def parse():
                     help="after the timed steps, also time the same step with strided-B heads in the residue view "
                          "and fixed-B heads in the compact view (reported as views_path; off by default so that a "
                          "kernel trace of the default command holds only the timed launches)")
+    ap.add_argument("--batch", type=int, default=0, help="override the workload's batch (exploration)")
+    ap.add_argument("--heads", type=int, default=0, help="override the workload's head count (exploration)")
+    ap.add_argument("--n", type=int, default=0, help="override the workload's sequence length (exploration)")
+    ap.add_argument("--split", type=int, default=None,
+                    help="chunking of long lists for this run (sa_set_split: 0 per call, -1 none, k > 0 forced)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-heads", type=int, default=0,
                     help="heads in the oracle sample (default: sized to ~10-30 s)")
@@ -486,6 +491,14 @@ def main():
     import workloads
 
     w = workloads.WORKLOADS[args.workload]
+    shape_tag = ""
+    if args.batch or args.heads or args.n:
+        import dataclasses
+        w = dataclasses.replace(w, batch=args.batch or w.batch, heads=args.heads or w.heads, n=args.n or w.n)
+        shape_tag = "-b%dh%dn%d" % (w.batch, w.heads, w.n)
+    if args.split is not None:
+        sa.sa_set_split(args.split)
+        shape_tag += "-split%d" % args.split
     dev = torch.device("cuda:0")
     pats = w.head_patterns(dense=args.dense)
     T, d = w.block, w.d
@@ -503,7 +516,7 @@ def main():
         lays.append(cache[(p, l, c)])
     layout_ms = (time.perf_counter() - t0) * 1e3
 
-    label = (w.name + ("-dense" if args.dense else "") + ("-residue-view" if args.residue_view else "")
+    label = (w.name + shape_tag + ("-dense" if args.dense else "") + ("-residue-view" if args.residue_view else "")
              + ("-compact-view" if args.compact_view else ""))
     views = args.residue_view or args.compact_view
     x = workloads.make_inputs(w)
