@@ -130,12 +130,16 @@ size_t plan_key(char* buf, size_t cap, ListKind kind, int dev, int32_t B, int32_
 // list, the longest-first order leaves their loads even and chunks only add
 // work (their partial results and the combining pass).  Chunks pay where one
 // list is longer than the other units' whole loads -- few heads and a batch
-// of one, where some units would idle: a list longer than twice the average
-// load of a unit is cut into chunks of that length (at least 16 steps).
-// Measured (one box, fwd + dQ + dK/dV): B = 1, two strided heads, n = 8192:
-// 149 -> 86 us; B = 1, two fixed heads, n = 16384: 381 -> 138 us; the five
-// workloads (every unit holding 12 to 100 times the longest list) unchanged
-// by this rule, and 2-35 % slower with chunks forced on.
+// of one, where some units would idle.  Lists are cut into chunks of about
+// the average load of a unit (at least 16 steps): in a call with at most
+// 1.25 lists per unit every list longer than that, else only lists longer
+// than twice the average.  Measured (one box, fwd + dQ + dK/dV, chunk
+// lengths forced): B = 1, two strided heads, n = 8192 (128 lists): 149 us
+// whole, 86 at 16 steps, 107 at 32; B = 1, two fixed heads, n = 16384 (256
+// lists): 381 us whole, 138 at 32, 187 at 64 -- the best lengths are the
+// average loads (9 and 33 steps, 16 at least); img32 (384 lists, the longest
+// 1.9 times the average) 118 us whole, 125-130 with chunks of 12-16; the
+// five workloads get no chunks (2-35 % slower with chunks forced on).
 int32_t plain_chunk(ListKind kind, int dev, int32_t B, int32_t H, sa_layout* const* hl, int split, int32_t* min_len)
 {
     *min_len = 0;
@@ -146,15 +150,20 @@ int32_t plain_chunk(ListKind kind, int dev, int32_t B, int32_t H, sa_layout* con
     }
     int cus = 0;
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) return 0;
-    int64_t total = 0;
+    int64_t total = 0, lists = 0;
     for (int32_t h = 0; h < H; ++h) {
         const std::vector<int32_t>& ptr = kind == kByKeyPair ? hl[h]->kgroups.ptr : hl[h]->qgroups.ptr;
-        if (!ptr.empty()) total += (int64_t)(ptr.back() - ptr.front()) * hl[h]->view_l;
+        if (ptr.empty()) continue;
+        total += (int64_t)(ptr.back() - ptr.front()) * hl[h]->view_l;
+        lists += (int64_t)(ptr.size() - 1) * hl[h]->view_l;
     }
     total *= B;
-    const double cs = std::max(16.0, std::ceil(2.0 * (double)total / (double)cus));
-    if (cs > (double)(1 << 30)) return 0;
-    *min_len = (int32_t)cs;
+    lists *= B;
+    const double avg = (double)total / (double)cus;
+    const double cs = std::max(16.0, std::ceil(avg));
+    const double over = 4 * lists <= 5 * (int64_t)cus ? cs : std::max(cs, std::ceil(2.0 * avg));
+    if (over > (double)(1 << 30)) return 0;
+    *min_len = (int32_t)over;
     return (int32_t)cs;
 }
 

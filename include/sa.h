@@ -351,10 +351,11 @@ int sa_set_fwd_form(int form);
  * deterministic (fixed order, no atomics) and equal to those of an
  * unchunked walk up to rounding order.  Residue views are never chunked;
  * compact views' dK/dV chunks (96 steps) are not affected.
- *   0   chosen per call (default): lists longer than twice the average
- *       number of steps per compute unit (at least 16) are cut into chunks
- *       of that length; calls whose every unit holds many lists' worth of
- *       steps get no chunks
+ *   0   chosen per call (default): lists are cut into chunks of about
+ *       the average number of steps per compute unit (at least 16): in a
+ *       call with at most 1.25 lists per unit every list longer than that,
+ *       else lists longer than twice that average; calls whose every unit
+ *       holds many lists' worth of steps get no chunks
  *   -1  no chunks
  *   k>0 every list longer than k steps in ceil(len / k) near-equal chunks
  * *previous (if not NULL) receives the setting before the call.  Returns
