@@ -253,6 +253,30 @@ def test_more_than_eight_layouts_rejected():
     assert b"distinct" in lib.sa_last_error()
 
 
+def test_process_switches_validate_and_restore():
+    """The process-wide test and tuning switches (no GPU needed): each
+    returns the setting it replaces, refuses values outside its range with
+    SA_ERR_INVALID_ARG and leaves the setting unchanged then."""
+    lib = sa.library()
+    prev = ctypes.c_int(-7)
+    assert lib.sa_set_split(5, ctypes.byref(prev)) == sa.SA_OK and prev.value == 0
+    assert lib.sa_set_split(-2, ctypes.byref(prev)) == sa.SA_ERR_INVALID_ARG
+    assert b"below -1" in lib.sa_last_error()
+    assert lib.sa_set_split(-1, ctypes.byref(prev)) == sa.SA_OK and prev.value == 5
+    assert lib.sa_set_split(0, None) == sa.SA_OK
+    assert sa.sa_set_split(0) == 0
+    assert lib.sa_set_one_paths(0, ctypes.byref(prev)) == sa.SA_OK and prev.value == 1
+    assert lib.sa_set_one_paths(2, ctypes.byref(prev)) == sa.SA_ERR_INVALID_ARG
+    assert sa.sa_set_one_paths(True) is False
+    assert sa.sa_set_one_paths(True) is True
+    with pytest.raises(sa.SAError):
+        sa.sa_set_split(-3)
+    assert sa.sa_set_fwd_form("half") == "auto"
+    with pytest.raises(sa.SAError):
+        sa.sa_set_fwd_form(3)
+    assert sa.sa_set_fwd_form("auto") == "half"
+
+
 def test_status_strings():
     lib = sa.library()
     for code in (sa.SA_OK, sa.SA_ERR_INVALID_ARG, sa.SA_ERR_UNSUPPORTED, sa.SA_ERR_HIP, sa.SA_ERR_ALLOC):
