@@ -750,6 +750,16 @@ def test_random_sweep_matches_oracle(case):
             compare_head(x, res, b, h, pats[h], scale, True, fp32=False)
 
 
+@pytest.mark.parametrize("case", _sweep_cases(count=16, seed=2020), ids=lambda c: "chunked%d" % c[0])
+def test_random_sweep_chunked_matches_oracle(case, split_steps):
+    """Seeded random configurations with every list longer than 1 to 5 steps
+    walked in chunks (combining passes after each kernel) against the
+    oracle, all outputs."""
+    idx = case[0]
+    split_steps(1 + idx % 5)
+    test_random_sweep_matches_oracle(case)
+
+
 def test_destroy_releases_work_lists():
     """Destroying a layout frees the cached work lists of the calls that used
     it: building, using and destroying fresh layouts over and over leaves the
