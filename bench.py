@@ -43,10 +43,11 @@ def parse():
     ap.add_argument("--compact-view", action="store_true",
                     help="run fixed-B heads in their compact view (blocks of the summary keys only); the "
                          "metric then counts the compact view's blocks")
-    ap.add_argument("--views-path", action="store_true",
-                    help="after the timed steps, also time the same step with strided-B heads in the residue view "
-                         "and fixed-B heads in the compact view (reported as views_path; off by default so that a "
-                         "kernel trace of the default command holds only the timed launches)")
+    ap.add_argument("--no-views-path", action="store_true",
+                    help="skip the views path: by default, after the timed steps, the same step is also timed with "
+                         "strided-B heads in the residue view and fixed-B heads in the compact view (reported as "
+                         "views_path; its launches have other grid sizes than the timed ones, which is how a "
+                         "kernel trace tells them apart)")
     ap.add_argument("--batch", type=int, default=0, help="override the workload's batch (exploration)")
     ap.add_argument("--heads", type=int, default=0, help="override the workload's head count (exploration)")
     ap.add_argument("--n", type=int, default=0, help="override the workload's sequence length (exploration)")
@@ -598,7 +599,7 @@ def main():
     kern_file = "fwd.hip" if dominant == "fwd" else "bwd.hip"
     # The fastest walk of the same pairs, when the layouts have views (after
     # the timed steps, on its own buffers).
-    fastest = views_step(w, pats, x, max(5, args.steps // 2), 3) if args.views_path and not views else None
+    fastest = views_step(w, pats, x, max(5, args.steps // 2), 3) if not args.no_views_path and not views else None
     # The machine's own denominators, measured after the timed steps.
     mp = measured_peaks() if w.dtype == "bf16" else None
     mpeak = mp["mfma_bf16_tflops"] if mp else None
