@@ -168,12 +168,12 @@ int32_t plain_chunk(ListKind kind, int dev, int32_t B, int32_t H, sa_layout* con
 }
 
 // The work list of a call, built and uploaded on first use, with the
-// partial-result buffer of `stream`.  create = false: only look them up (no
-// allocation); SA_ERR_UNSUPPORTED when the list is not cached.  A stream
-// with no buffer of its own gets one, unless nothing may be allocated
-// (create = false) or the stream is being captured into a graph: then a
-// buffer made for another stream serves (calls that share it must not
-// overlap), and SA_ERR_UNSUPPORTED when there is none.
+// partial-result buffer of `stream`.  create = false (nothing may be
+// allocated: sa_bwd_noalloc, or a stream being captured into a graph): only
+// look them up; SA_ERR_UNSUPPORTED when the list is not cached.  A stream
+// with no buffer of its own gets one, unless create = false: then a buffer
+// made for another stream serves (calls that share it must not overlap),
+// and SA_ERR_UNSUPPORTED when there is none.
 int get_plan(ListKind kind, int dev, int32_t B, int32_t H, int32_t d, sa_layout* const* hl, void* stream, Plan* out,
              bool create)
 {
@@ -184,8 +184,8 @@ int get_plan(ListKind kind, int dev, int32_t B, int32_t H, int32_t d, sa_layout*
     auto it = g_plans.find(std::string_view(kbuf, klen));
     if (it == g_plans.end()) {
         if (!create)
-            return fail(SA_ERR_UNSUPPORTED, "no cached work list for this (B, H, layouts) on device %d (one call of "
-                        "sa_bwd with the same arguments caches it)", dev);
+            return fail(SA_ERR_UNSUPPORTED, "no cached work list for this (B, H, layouts) on device %d (one "
+                        "uncaptured call of the same kind with the same arguments caches it)", dev);
         const std::string key(kbuf, klen);
         int32_t min_len = 0;
         const int32_t cs = plain_chunk(kind, dev, B, H, hl, split, &min_len);
@@ -244,10 +244,7 @@ int get_plan(ListKind kind, int dev, int32_t B, int32_t H, int32_t d, sa_layout*
     if (pe.plan.part_bytes) {
         auto b = pe.parts.find(stream);
         if (b == pe.parts.end()) {
-            hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
-            if (create && hipStreamIsCapturing((hipStream_t)stream, &cs) != hipSuccess)
-                cs = hipStreamCaptureStatusNone;
-            if (!create || cs != hipStreamCaptureStatusNone) {
+            if (!create) {
                 if (pe.parts.empty())
                     return fail(SA_ERR_UNSUPPORTED, "no partial-result buffer for this work list on device %d yet "
                                 "(one uncaptured call on the device makes it)", dev);
@@ -288,6 +285,15 @@ void release_plans(uint64_t serial)
 }
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15) == 0; }
+
+// Whether `stream` is being captured into a graph: a captured call must not
+// allocate or copy synchronously, so it only looks up what an earlier
+// uncaptured call left on the device.
+bool capturing(void* stream)
+{
+    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+    return hipStreamIsCapturing((hipStream_t)stream, &cs) == hipSuccess && cs != hipStreamCaptureStatusNone;
+}
 
 // Checks shared by sa_fwd and sa_bwd; fills the head table with the layouts
 // the kernels walk (a layout's view when it has one).
@@ -498,10 +504,11 @@ int sa_fwd(const sa_layout_t* const* head_layout, int32_t B, int32_t H, int64_t 
     if (!q || !k || !v || !o || !lse) return fail(SA_ERR_INVALID_ARG, "sa_fwd: NULL tensor pointer");
     if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || ((uintptr_t)lse & 3))
         return fail(SA_ERR_INVALID_ARG, "sa_fwd: q, k, v, o must be 16-byte aligned, lse 4-byte aligned");
-    st = prepare_device(distinct, nl, &ht, &dev, true);
+    const bool alloc = !capturing(stream);
+    st = prepare_device(distinct, nl, &ht, &dev, alloc);
     if (st != SA_OK) return st;
     Plan plan;
-    st = get_plan(dtype == SA_BF16 ? kByQueryPair : kByQuery, dev, B, H, d, hl, stream, &plan, true);
+    st = get_plan(dtype == SA_BF16 ? kByQueryPair : kByQuery, dev, B, H, d, hl, stream, &plan, alloc);
     if (st != SA_OK) return st;
     FwdArgs a;
     a.q = q;
@@ -595,6 +602,7 @@ int bwd_call(const char* fn, int stages, const sa_layout_t* const* head_layout, 
     if (ws_bytes < sa_bwd_workspace_size(B, H, n, d))
         return fail(SA_ERR_INVALID_ARG, "%s: workspace of %zu bytes, %zu needed", fn, ws_bytes,
                     sa_bwd_workspace_size(B, H, n, d));
+    alloc = alloc && !capturing(stream);
     st = prepare_device(distinct, nl, &ht, &dev, alloc);
     if (st != SA_OK) return st;
     Plan pk{}, pq{};

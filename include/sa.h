@@ -52,7 +52,10 @@
  * combination allocates and uploads a small work list (synchronously), as
  * does the first use of a layout on a device; later calls reuse them and
  * only enqueue kernels, so they may be captured into a HIP graph (make one
- * uncaptured call of each kind first).  Calls are thread-safe.
+ * uncaptured call of each kind first: a call on a stream being captured
+ * allocates and copies nothing, and returns SA_ERR_UNSUPPORTED, with nothing
+ * enqueued, when its layouts or work list are not on the device yet).  Calls
+ * are thread-safe.
  *
  * Compiled (dtype, block, d) combinations:
  *     forward   (SA_F32, 16, 64), (SA_BF16, 64, 64), (SA_BF16, 64, 128)
@@ -221,10 +224,11 @@ void sa_layout_destroy(sa_layout_t* lay);
  * walked in chunks (sa_set_split).  The work list of (head_layout, B, H, d)
  * is built and kept on the device on the first call, with a partial-result
  * buffer per stream that runs it; calls on different streams may overlap.
- * Under graph capture nothing is allocated: a stream being captured that
- * has no buffer of its own uses one made for another stream by an earlier
- * uncaptured call (SA_ERR_UNSUPPORTED if there is none), and the captured
- * work must not overlap that stream's calls.
+ * Under graph capture nothing is allocated: the layouts and the work list
+ * must be on the device already (else SA_ERR_UNSUPPORTED), and a stream
+ * being captured that has no buffer of its own uses one made for another
+ * stream by an earlier uncaptured call (SA_ERR_UNSUPPORTED if there is
+ * none); the captured work must not overlap that stream's calls.
  */
 int sa_fwd(const sa_layout_t* const* head_layout, int32_t B, int32_t H, int64_t n, int32_t d,
            int dtype, float scale, const void* q, const void* k, const void* v, void* o,

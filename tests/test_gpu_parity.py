@@ -828,6 +828,55 @@ def test_graph_capture_replays(steps, split_steps):
         torch.cuda.synchronize()
 
 
+@pytest.mark.filterwarnings("ignore:The CUDA Graph is empty")  # the refused capture holds nothing
+def test_capture_before_any_call_is_refused():
+    """A call on a stream being captured allocates and copies nothing: with
+    layouts that no call has put on the device yet, sa_fwd and sa_bwd return
+    SA_ERR_UNSUPPORTED and enqueue nothing, and the capture stays usable;
+    after one uncaptured call the same capture replays the eager results."""
+    n = 768
+    pats = [("strided_a", 64, 1), ("fixed_b", 64, 16)]
+    x = workloads.custom_inputs((1, 2, n, 64), torch.bfloat16, seed=37)
+    lays = layouts_for(pats, n, 64)  # fresh layouts: nothing on the device
+    q, k, v, do = (x[t].to(DEV) for t in ("q", "k", "v", "do"))
+    o, lse = torch.empty_like(q), torch.empty(q.shape[:3], dtype=torch.float32, device=DEV)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(q), torch.empty_like(q)
+    ws = torch.empty(sa.sa_bwd_workspace_size(1, 2, n, 64), dtype=torch.uint8, device=DEV)
+
+    def capture():
+        g = torch.cuda.CUDAGraph()
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        errs = []
+        with torch.cuda.stream(s):
+            with torch.cuda.graph(g, stream=s):
+                for call in (lambda: sa.sa_fwd(q, k, v, lays, 1.0, o=o, lse=lse),
+                             lambda: sa.sa_bwd(q, k, v, o, lse, do, lays, 1.0, dq=dq, dk=dk, dv=dv, workspace=ws)):
+                    try:
+                        call()
+                    except sa.SAError as e:
+                        errs.append(e.status)
+        torch.cuda.synchronize()
+        return g, errs
+
+    torch.cuda.synchronize()
+    _, errs = capture()
+    assert errs == [sa.SA_ERR_UNSUPPORTED, sa.SA_ERR_UNSUPPORTED]
+    ref_o, ref_lse = sa.sa_fwd(q, k, v, lays, 1.0)
+    ref = sa.sa_bwd(q, k, v, ref_o, ref_lse, do, lays, 1.0)
+    torch.cuda.synchronize()
+    g, errs = capture()
+    assert errs == []
+    for t in (o, dq, dk, dv):
+        t.fill_(float("nan"))
+    torch.cuda.synchronize()
+    g.replay()
+    torch.cuda.synchronize()
+    assert torch.equal(o, ref_o) and torch.equal(lse, ref_lse)
+    for got, want, nm in zip((dq, dk, dv), ref, ("dq", "dk", "dv")):
+        assert torch.equal(got, want), nm
+
+
 # ---------------------------------------------------------------------------
 # Long lists walked in chunks (sa_set_split): partial results combined in
 # list order by a second kernel per stage.
