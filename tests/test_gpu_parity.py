@@ -211,6 +211,24 @@ def test_edge_cases(case):
             compare_head(x, res, b, h, pats[h], 1.0, True, fp32=False)
 
 
+def test_most_heads_and_layouts_in_one_call():
+    """The largest call the head table holds: 256 heads over 8 distinct
+    layouts (every pattern, views among them), forward and backward, every
+    head against the oracle."""
+    n, d = 256, 64
+    pats = [("strided_a", 64, 1), ("strided_b", 64, 1), ("fixed_a", 64, 16), ("fixed_b", 64, 16),
+            ("dense", 1, 1), ("strided_a", 3, 1), ("strided_b", 32, 1), ("fixed_b", 128, 4)]
+    base = layouts_for(pats, n, 64)
+    base[6].set_residue_view(True)   # strided B, l = 32: 8-row residue classes
+    base[7].set_compact_view(True)   # fixed B, c = 4
+    H = 256
+    heads = [pats[h % 8] for h in range(H)]
+    x = workloads.custom_inputs((1, H, n, d), torch.bfloat16, seed=41)
+    res = run(x, heads, 64, 1.0, backward=True, lays=[base[h % 8] for h in range(H)])
+    for h in range(H):
+        compare_head(x, res, 0, h, heads[h], 1.0, True, fp32=False)
+
+
 def test_fixed_b_empty_rows_exact():
     """Rows with no allowed key: O = 0 and lse = -inf exactly, zero gradients."""
     n, l, c = 512, 128, 32

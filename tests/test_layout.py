@@ -204,6 +204,12 @@ def test_fwd_bwd_argument_errors_without_gpu():
     # too small a workspace
     st = lib.sa_bwd(h, 1, 2, 256, 64, sa.SA_BF16, 1.0, p, p, p, p, p, p, p, p, p, p, 16, None)
     assert st == sa.SA_ERR_INVALID_ARG
+    # nine distinct layouts in one call (at most eight)
+    nine = [sa.sa_layout_build("strided_a", 256, 1 + i, block=64) for i in range(9)]
+    st = lib.sa_fwd(_heads(*nine), 1, 9, 256, 64, sa.SA_BF16, 1.0, p, p, p, p, p, None)
+    assert st == sa.SA_ERR_INVALID_ARG and b"distinct" in lib.sa_last_error()
+    st = lib.sa_bwd(_heads(*nine), 1, 9, 256, 64, sa.SA_BF16, 1.0, p, p, p, p, p, p, p, p, p, p, 1 << 20, None)
+    assert st == sa.SA_ERR_INVALID_ARG
     # NULL layout entry
     hn = (ctypes.c_void_p * 2)(lay.handle, None)
     st = lib.sa_fwd(hn, 1, 2, 256, 64, sa.SA_BF16, 1.0, p, p, p, p, p, None)
