@@ -71,3 +71,47 @@ def test_noalloc_rejects_beyond_scratch():
     st = lib.sa_bwd_noalloc(heads, 1, 64, n, d, sa.SA_BF16, 1.0, *([ctypes.c_void_p(16)] * 9), None)
     assert st == sa.SA_ERR_INVALID_ARG
     assert b"scratch" in lib.sa_last_error()
+
+
+@pytest.mark.parametrize("steps", [0, 3])
+def test_noalloc_captured_replays(steps, split_steps):
+    """The callers this entry point is for include graph capture: captured
+    after one sa_bwd, every replay gives sa_bwd's results bit for bit, also
+    with other calls on the same scratch array between the replays."""
+    split_steps(steps)
+    (B, H, n, d, pats, seed), (B2, H2, n2, d2, pats2, seed2) = CALLS
+    lays = [sa.sa_layout_build(p, n, l, c, block=64) for (p, l, c) in pats]
+    x = workloads.custom_inputs((B, H, n, d), torch.bfloat16, seed=seed)
+    q, k, v, do = (x[t].to(DEV) for t in ("q", "k", "v", "do"))
+    o, lse = sa.sa_fwd(q, k, v, lays, 1.0)
+    ref = sa.sa_bwd(q, k, v, o, lse, do, lays, 1.0)
+    # a smaller call of its own, run eagerly between the replays
+    lays2 = [sa.sa_layout_build(p, n2, l, c, block=64) for (p, l, c) in pats2]
+    x2 = workloads.custom_inputs((B2, H2, n2, d2), torch.bfloat16, seed=seed2)
+    q2, k2, v2, do2 = (x2[t].to(DEV) for t in ("q", "k", "v", "do"))
+    o2, lse2 = sa.sa_fwd(q2, k2, v2, lays2, 1.0)
+    ref2 = sa.sa_bwd(q2, k2, v2, o2, lse2, do2, lays2, 1.0)
+    # (an uncaptured call first: it finds the scratch array's address)
+    sa.sa_bwd_noalloc(q2, k2, v2, o2, lse2, do2, lays2, 1.0, *(torch.empty_like(q2) for _ in range(3)))
+    dq, dk, dv = (torch.empty_like(q) for _ in range(3))
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            sa.sa_bwd_noalloc(q, k, v, o, lse, do, lays, 1.0, dq, dk, dv)
+    torch.cuda.synchronize()
+    for rep in range(3):
+        for t in (dq, dk, dv):
+            t.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for got, want, nm in zip((dq, dk, dv), ref, ("dq", "dk", "dv")):
+            assert torch.equal(got, want), (rep, nm)
+        g2 = [torch.full_like(q2, float("nan")) for _ in range(3)]
+        sa.sa_bwd_noalloc(q2, k2, v2, o2, lse2, do2, lays2, 1.0, *g2)
+        torch.cuda.synchronize()
+        for got, want, nm in zip(g2, ref2, ("dq", "dk", "dv")):
+            assert torch.equal(got, want), (rep, "eager", nm)
